@@ -1,0 +1,113 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check a pin catches each.
+
+Every case monkeypatches one oracle function with a subtly wrong variant and
+runs the pins that should reject it; the test passes only if one of them fails.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from tests import test_oracle_pins as P
+
+
+def _rope_interleaved(x, pos, base=10000.0):
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    h = n // 2
+    pos = np.asarray(pos, dtype=np.float64)[..., None]
+    th = pos * np.power(base, -np.arange(h) / h)
+    c, s = np.cos(th), np.sin(th)
+    y = x.copy()
+    y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    y[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * s
+    return y
+
+
+def _rope_sign(x, pos, base=10000.0):
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    pos = np.asarray(pos, dtype=np.float64)[..., None]
+    th = pos * np.power(base, -np.arange(h) / h)
+    c, s = np.cos(th), np.sin(th)
+    lo, hi = x[..., :h], x[..., h:]
+    return np.concatenate([lo * c + hi * s, hi * c - lo * s], -1)
+
+
+def _rope_freq(x, pos, base=10000.0):
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    h = n // 2
+    pos = np.asarray(pos, dtype=np.float64)[..., None]
+    th = pos * np.power(base, -np.arange(h) / n)
+    c, s = np.cos(th), np.sin(th)
+    lo, hi = x[..., :h], x[..., h:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], -1)
+
+
+_orig_absorbed = O.attend_absorbed
+
+
+def _absorbed_no_rope_term(q_b, rows, n_q, d_latent, scale):
+    q = np.array(q_b, dtype=np.float64)
+    q[..., d_latent:] = 0
+    return _orig_absorbed(q, rows, n_q, d_latent, scale)
+
+
+def _combine_unweighted(o_parts, lse_parts):
+    o = np.asarray(o_parts, dtype=np.float64)
+    l = np.asarray(lse_parts, dtype=np.float64)
+    return o.mean(0), l.max(0)
+
+
+def _encode_no_saturation(x):
+    import torch
+    t = __import__("torch").as_tensor(np.asarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+MUTANTS = {
+    "rope_interleaved_pairs": ("rope", _rope_interleaved,
+                               [P.test_rope_pairs_channel_j_with_j_plus_half]),
+    "rope_sign_flip": ("rope", _rope_sign, [P.test_rope_two_dims_is_textbook_rotation]),
+    "rope_freq_over_n": ("rope", _rope_freq, [P.test_rope_pairs_channel_j_with_j_plus_half]),
+    "scale_over_full_row": ("softmax_scale", lambda dn, dr: 1.0 / math.sqrt(dn + 2 * dr + 8),
+                            [P.test_unabsorbed_matches_library_attention]),
+    "query_excludes_itself": ("visible", lambda L, n_q, j: L - n_q + j,
+                              [P.test_decode_special_cases,
+                               P.test_unabsorbed_matches_library_attention]),
+    "dropped_rope_score_term": ("attend_absorbed", _absorbed_no_rope_term,
+                                [P.test_unabsorbed_matches_library_attention]),
+    "out_proj_transposed": ("out_proj", lambda u, w: np.einsum("rid,idv->riv", np.asarray(u),
+                                                               np.asarray(w).transpose(0, 1, 2)),
+                            [P.test_out_proj_explicit_loops]),
+    "combine_unweighted": ("combine", _combine_unweighted,
+                           [P.test_combine_of_any_partition_equals_unsplit]),
+    "fp8_no_saturation": ("e4m3_encode", _encode_no_saturation,
+                          [P.test_e4m3_encode_round_trip_ties_and_saturation]),
+    "fp8_scale_off": ("E4M3_MAX", 447.0, [P.test_fp8_row_quantizer_properties]),
+    "bf16_truncation": ("to_bf16_bits",
+                        lambda x: (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16),
+                        [P.test_bf16_rounding_known_values]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, repl, pins = MUTANTS[name]
+    monkeypatch.setattr(O, attr, repl)
+    caught = False
+    for pin in pins:
+        try:
+            if "n" in pin.__code__.co_varnames[:pin.__code__.co_argcount]:
+                pin(8)
+            elif "n_q" in pin.__code__.co_varnames[:pin.__code__.co_argcount]:
+                pin(2)
+            elif "dtype" in pin.__code__.co_varnames[:pin.__code__.co_argcount]:
+                pin("fp32")
+            else:
+                pin()
+        except Exception:
+            caught = True
+    assert caught, f"no pin rejected the planted mistake {name}"
