@@ -1,0 +1,177 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA latent-cache decode library.
+ *
+ * Multi-head latent attention (MLA) decode in the matrix-absorbed form over a
+ * paged latent cache, as described on the page "DeepSeek MLA Architecture:
+ * How Multi-Head Latent Attention Cuts KV Cache by 93%" (below: [MLA-93]),
+ * sections "Core Mechanics" 1-3, "Total Cached Scalars per Token" and the
+ * single-token decoding listing, and on "DeepSeek-V3 Architecture: Multi-Head
+ * Latent Attention (MLA) & FP8 Mixed-Precision Training" (below: [V3-ARCH]),
+ * sections 2, A and 3.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them, and keeps no per-call state.
+ *  - Every call only validates its arguments on the host and enqueues work on
+ *    `stream` (a hipStream_t; NULL = the default stream).  Nothing is
+ *    synchronised; outputs are ready when the stream reaches that point.
+ *  - Return value: MLA_OK (0) or a negative mla_status.  On error nothing has
+ *    been enqueued (except MLA_ERR_HIP, where a launch itself failed) and
+ *    mla_last_error() returns a description (thread-local).  No exception or
+ *    abort crosses the ABI.
+ *  - Row-major layouts; the last index is contiguous.
+ *  - Cache layout (paged): `cache` is [num_blocks][block_size][D] with
+ *    D = d_latent + d_rope; row = [c^KV (d_latent) ; k^R (d_rope)], the
+ *    latent first.  Token at logical position p of sequence b lives in
+ *    physical block page_table[b * max_blocks_per_seq + p / block_size], row
+ *    p % block_size.  For the fp8 cache `cache_scales` is
+ *    [num_blocks][block_size][n_tiles] fp32 with n_tiles = ceil(D / 128):
+ *    element x of tile k (channels [128k, min(128k+128, D))) decodes to
+ *    e4m3(x) * scale[k]  (tile-level scaling as in the FP8 paragraph of
+ *    "DeepSeek Unveils DualPipe & Multi-Head Latent Attention").
+ *  - Device-data preconditions (not checked unless noted): page-table entries
+ *    that a call reads are in [0, num_blocks); n_q <= seq_lens[b] <=
+ *    max_blocks_per_seq * block_size.  Entries that are never read may hold
+ *    anything (e.g. -1).  Cache rows past seq_lens[b] are never used, whatever
+ *    they hold (NaN included).
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef void *mla_stream_t; /* a hipStream_t */
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, inconsistent dims */
+  MLA_ERR_UNSUPPORTED = -2,      /* no kernel for this dims/dtype combination */
+  MLA_ERR_WORKSPACE_TOO_SMALL = -3,
+  MLA_ERR_HIP = -4               /* a HIP runtime call or launch failed */
+} mla_status;
+
+typedef enum mla_dtype {
+  MLA_FP32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2 /* OCP E4M3 (max 448, no infinities); cache only */
+} mla_dtype;
+
+/* Model dimensions, shared by every call.
+ * [MLA-93] Core Mechanics 1 and 3: d_latent = d_c (512 for DeepSeek-V3),
+ * d_rope = d_R (64), d_nope = per-head content width (128), d_v = per-head
+ * value width (128), num_heads = H (128). */
+typedef struct mla_dims {
+  int32_t num_heads;
+  int32_t d_latent;
+  int32_t d_rope;      /* even */
+  int32_t d_nope;      /* used only for the default softmax scale */
+  int32_t d_v;
+  int32_t block_size;  /* tokens per cache block, > 0 */
+  int32_t cache_dtype; /* mla_dtype of the cache */
+  int32_t act_dtype;   /* mla_dtype of q, h, weights, u, o: MLA_FP32 or MLA_BF16 */
+  float softmax_scale; /* <= 0 selects 1/sqrt(d_nope + d_rope) */
+  float rope_base;     /* <= 0 selects 10000 */
+  int32_t flags;       /* bitwise OR of MLA_FLAG_*; 0 for defaults */
+} mla_dims;
+
+/* Use the generic VALU decode kernel even where the MFMA kernel applies
+ * (an independent second implementation, for cross-checks). */
+#define MLA_FLAG_GENERIC_DECODE 1
+
+int mla_abi_version(void);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char *mla_last_error(void);
+
+/* Number of compute units of the current device (0 on failure). */
+int mla_device_cu_count(void);
+
+/*
+ * mla_cache_append -- project, rotate and store new tokens' cache rows.
+ * [MLA-93] Core Mechanics 1 (c = W^DKV h) and 3 (k^R = RoPE(W^KR h), shared
+ * by all heads); decoding listing STEP 1.  RoPE is rotate-half: channel j of
+ * k^R is paired with j + d_rope/2 and rotated by pos * base^(-j/(d_rope/2)).
+ *
+ *   h          [n_tokens][d_model]        act_dtype
+ *   w_dkv      [d_latent][d_model]        act_dtype
+ *   w_kr       [d_rope][d_model]          act_dtype
+ *   seq_ids    [n_tokens] int32           sequence of each token
+ *   positions  [n_tokens] int32           logical position of each token (>= 0)
+ *   page_table [batch][max_blocks_per_seq] int32
+ *   cache      pool (see conventions), written only at the tokens' slots
+ *   cache_scales  fp8 only (else NULL): written for the same slots
+ * Accumulation is fp32; the row is stored in cache_dtype (bf16: RNE; fp8:
+ * per-tile amax scaling, scale = amax/448, code = e4m3_rne_sat(x * (448/amax)),
+ * scale 1 and zero codes for an all-zero tile).  Two tokens mapping to the same
+ * slot in one call is undefined.  Supported: any dims whose RoPE part lies in
+ * one 128-channel tile (true for d_latent = 512, d_rope = 64).
+ */
+int mla_cache_append(const mla_dims *dims, const void *h, int32_t n_tokens, int32_t d_model,
+                     const void *w_dkv, const void *w_kr, const int32_t *seq_ids,
+                     const int32_t *positions, const int32_t *page_table,
+                     int32_t max_blocks_per_seq, void *cache, float *cache_scales,
+                     mla_stream_t stream);
+
+/*
+ * Split-KV decode (mla_decode + mla_decode_combine).
+ *
+ * q [batch][n_q][num_heads][d_latent + d_rope] act_dtype: packed absorbed
+ * queries [q~ ; q^R], q~_i = (W^UK_i)^T q^C_i, q^R already rotated at the
+ * query position ([MLA-93] Core Mechanics 3).  Query j of sequence b sits at
+ * position seq_lens[b] - n_q + j and attends to positions
+ * 0 .. seq_lens[b] - n_q + j (itself included: the new tokens are appended
+ * before attention, decoding listing STEP 1 then STEP 4).  Per head i:
+ *   s_t = scale * (q~_i . c_t + q^R_i . k^R_t),  p = softmax_t(s),
+ *   u_i = sum_t p_t c_t  in R^{d_latent}        (listing STEPs 4-5).
+ *
+ * The cache blocks of all sequences are laid end to end and cut into
+ * `num_partitions` near-equal ranges; one workgroup per (range, query token)
+ * walks its range and writes, for every sequence piece it covers, a partial
+ * (o = normalised latent output, lse = natural-log sum of exp of the scores)
+ * into `workspace`.  mla_decode_combine merges the pieces of each sequence
+ * with a log-sum-exp weighting.  num_partitions <= 0 selects the default
+ * (the device's compute-unit count divided by n_q, at least 1).  Results are
+ * deterministic for a fixed num_partitions.
+ */
+size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch, int32_t n_q,
+                                 int32_t num_partitions);
+
+int mla_decode(const mla_dims *dims, const void *q, int32_t batch, int32_t n_q,
+               const void *cache, const float *cache_scales, const int32_t *page_table,
+               int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_partitions,
+               void *workspace, size_t workspace_bytes, mla_stream_t stream);
+
+/* Merge the partials written by the preceding mla_decode with the same
+ * arguments: per (b, j, head) M = max_s lse_s, w_s = exp(lse_s - M),
+ * u = sum_s w_s o_s / sum_s w_s, lse = M + ln sum_s w_s.
+ *   u_out   [batch][n_q][num_heads][d_latent] act_dtype
+ *   lse_out [batch][n_q][num_heads] fp32, may be NULL */
+int mla_decode_combine(const mla_dims *dims, const void *workspace, size_t workspace_bytes,
+                       int32_t batch, int32_t n_q, const int32_t *seq_lens,
+                       int32_t num_partitions, void *u_out, float *lse_out,
+                       mla_stream_t stream);
+
+/*
+ * mla_out_proj -- per-head value up-projection o_i = W^UV_i u_i.
+ * [MLA-93] decoding listing STEP 5 (W^UV applied to the latent output).
+ *   u     [rows][num_heads][d_latent] act_dtype  (rows = batch * n_q)
+ *   w_uv  [num_heads][d_v][d_latent]  act_dtype
+ *   out   [rows][num_heads][d_v]      act_dtype
+ * fp32 accumulation.
+ */
+int mla_out_proj(const mla_dims *dims, const void *u, int32_t rows, const void *w_uv, void *out,
+                 mla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,192 @@
+// Generic split-KV decode over the paged latent cache (VALU, any dims/dtypes).
+//
+// One workgroup per (partition g, query token j, head i).  For every piece of
+// its partition it runs an online softmax over 64-token tiles:
+//   s_t = scale * (q~ . c_t + q^R . k^R_t)       ([MLA-93] Core Mechanics 3)
+//   u   = sum_t softmax(s)_t c_t                 (decoding listing STEPs 4-5)
+// and writes the piece's normalised output and log-sum-exp to the workspace.
+// This path serves small or unusual dims (and fp32), and is an independent
+// second GPU implementation for cross-checking the MFMA kernel.
+#include "mla_internal.h"
+
+namespace mla {
+
+constexpr int kGenNT = 256;
+constexpr int kGenTile = 64;  // tokens per tile (4 threads per token for scores)
+constexpr int kGenMaxD = 1024;
+
+template <int CDT>
+MLA_DEV float load_cache(const void* cache, const float* scales, int64_t row, int ch, int D,
+                         int ntiles) {
+  if constexpr (CDT == MLA_FP32) {
+    return static_cast<const float*>(cache)[row * D + ch];
+  } else if constexpr (CDT == MLA_BF16) {
+    return bf16_to_f32(static_cast<const uint16_t*>(cache)[row * D + ch]);
+  } else {
+    const uint8_t* c8 = static_cast<const uint8_t*>(cache);
+    return e4m3_to_f32(c8[row * D + ch]) * scales[row * ntiles + (ch >> 7)];
+  }
+}
+
+template <int ADT>
+MLA_DEV float load_act(const void* p, int64_t i) {
+  if constexpr (ADT == MLA_FP32)
+    return static_cast<const float*>(p)[i];
+  else
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+template <int CDT, int ADT>
+__global__ __launch_bounds__(kGenNT) void decode_generic_kernel(DecodeArgs a) {
+  __shared__ PlanScratch<kGenNT> plan;
+  __shared__ float qs[kGenMaxD];
+  __shared__ float ps[kGenTile];
+  __shared__ float red[kGenNT / kWave];
+
+  const int H = a.H, D = a.D, dc = a.d_latent, bs = a.block_size;
+  const int ntiles = (D + 127) / 128;
+  // blockIdx.x = (g * n_q + j) * H + i
+  const int i = blockIdx.x % H;
+  const int j = (blockIdx.x / H) % a.n_q;
+  const int g = blockIdx.x / (H * a.n_q);
+  const int tid = threadIdx.x;
+
+  plan_for_each_piece<kGenNT>(a.seq_lens, a.batch, bs, a.G, g, plan,
+                              [&](int b, int ulo, int uhi, int slot) {
+    const int L = a.seq_lens[b];
+    const int nvis = L - a.n_q + j + 1;  // positions 0 .. L - n_q + j
+    const int t_begin = ulo * bs;
+    const int t_end = min(uhi * bs, nvis);
+    const int64_t qoff = ((int64_t(b) * a.n_q + j) * H + i) * D;
+    __syncthreads();
+    for (int c = tid; c < D; c += kGenNT) qs[c] = load_act<ADT>(a.q, qoff + c);
+    __syncthreads();
+
+    float m = -INFINITY, l = 0.f;
+    float acc[kGenMaxD / kGenNT];
+#pragma unroll
+    for (int r = 0; r < kGenMaxD / kGenNT; ++r) acc[r] = 0.f;
+
+    for (int t0 = t_begin; t0 < t_end; t0 += kGenTile) {
+      // scores: 4 threads per token
+      const int tk = t0 + tid / 4, part = tid % 4;
+      float s = 0.f;
+      int64_t row = 0;
+      if (tk < t_end) {
+        row = int64_t(a.page_table[int64_t(b) * a.max_blocks + tk / bs]) * bs + tk % bs;
+        for (int c = part; c < D; c += 4) s += qs[c] * load_cache<CDT>(a.cache, a.scales, row, c, D, ntiles);
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      s = tk < t_end ? s * a.scale : -INFINITY;
+      const float tmax = block_max<kGenNT>(s, red);
+      const float m_new = fmaxf(m, tmax);
+      const float p = tk < t_end ? expf(s - m_new) : 0.f;
+      const float alpha = expf(m - m_new);  // 0 on the first tile (m = -inf)
+      if (part == 0) ps[tid / 4] = p;
+      const float psum = block_sum<kGenNT>(part == 0 ? p : 0.f, red);
+      l = l * alpha + psum;
+      m = m_new;
+      __syncthreads();
+      const int nt = min(kGenTile, t_end - t0);
+#pragma unroll
+      for (int r = 0; r < kGenMaxD / kGenNT; ++r) {
+        const int c = tid + r * kGenNT;
+        if (c < dc) {
+          float v = acc[r] * alpha;
+          for (int t = 0; t < nt; ++t) {
+            const int tt = t0 + t;
+            const int64_t rr = int64_t(a.page_table[int64_t(b) * a.max_blocks + tt / bs]) * bs + tt % bs;
+            v += ps[t] * load_cache<CDT>(a.cache, a.scales, rr, c, D, ntiles);
+          }
+          acc[r] = v;
+        }
+      }
+      __syncthreads();
+    }
+    const size_t obase = ((size_t(slot) * a.n_q + j) * H + i);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int r = 0; r < kGenMaxD / kGenNT; ++r) {
+      const int c = tid + r * kGenNT;
+      if (c < dc) a.ws_o[obase * dc + c] = acc[r] * inv;
+    }
+    if (tid == 0) a.ws_lse[obase] = l > 0.f ? m + logf(l) : -INFINITY;
+  });
+}
+
+template <int CDT, int ADT>
+static hipError_t launch_generic(const DecodeArgs& a, hipStream_t st) {
+  dim3 grid(unsigned(a.G) * a.n_q * a.H);
+  hipLaunchKernelGGL((decode_generic_kernel<CDT, ADT>), grid, dim3(kGenNT), 0, st, a);
+  return hipGetLastError();
+}
+
+bool decode_generic_supported(const DecodeArgs& a) { return a.D <= kGenMaxD; }
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
+  if (a.act_dtype == MLA_FP32) {
+    if (a.cache_dtype == MLA_FP32) return launch_generic<MLA_FP32, MLA_FP32>(a, st);
+    if (a.cache_dtype == MLA_BF16) return launch_generic<MLA_BF16, MLA_FP32>(a, st);
+    return launch_generic<MLA_FP8_E4M3, MLA_FP32>(a, st);
+  }
+  if (a.cache_dtype == MLA_FP32) return launch_generic<MLA_FP32, MLA_BF16>(a, st);
+  if (a.cache_dtype == MLA_BF16) return launch_generic<MLA_BF16, MLA_BF16>(a, st);
+  return launch_generic<MLA_FP8_E4M3, MLA_BF16>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of the pieces of each (sequence, query token, head).
+// One workgroup per (b, j) and group of kCombHeads heads.
+// ---------------------------------------------------------------------------
+constexpr int kCombNT = 256;
+constexpr int kCombHeads = 4;
+
+template <int ADT>
+__global__ __launch_bounds__(kCombNT) void combine_kernel(CombineArgs a) {
+  __shared__ PlanScratch<kCombNT> plan;
+  const int bj = blockIdx.x;
+  const int b = bj / a.n_q, j = bj % a.n_q;
+  const int h0 = blockIdx.y * kCombHeads;
+  int slot0, np;
+  plan_lookup<kCombNT>(a.seq_lens, a.batch, a.block_size, a.G, b, plan, &slot0, &np);
+  const int H = a.H, dc = a.d_latent;
+  for (int hh = 0; hh < kCombHeads; ++hh) {
+    const int h = h0 + hh;
+    if (h >= H) break;
+    float M = -INFINITY;
+    for (int s = 0; s < np; ++s) M = fmaxf(M, a.ws_lse[(size_t(slot0 + s) * a.n_q + j) * H + h]);
+    float wsum = 0.f;
+    for (int s = 0; s < np; ++s) {
+      const float ls = a.ws_lse[(size_t(slot0 + s) * a.n_q + j) * H + h];
+      wsum += ls == -INFINITY ? 0.f : expf(ls - M);
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const size_t orow = (size_t(b) * a.n_q + j) * H + h;
+    for (int c = threadIdx.x; c < dc; c += kCombNT) {
+      float acc = 0.f;
+      for (int s = 0; s < np; ++s) {
+        const size_t r = (size_t(slot0 + s) * a.n_q + j) * H + h;
+        const float ls = a.ws_lse[r];
+        if (ls != -INFINITY) acc += expf(ls - M) * a.ws_o[r * dc + c];
+      }
+      const float u = acc * inv;
+      if constexpr (ADT == MLA_FP32)
+        static_cast<float*>(a.u)[orow * dc + c] = u;
+      else
+        static_cast<uint16_t*>(a.u)[orow * dc + c] = f32_to_bf16(u);
+    }
+    if (threadIdx.x == 0 && a.lse_out) a.lse_out[orow] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+  dim3 grid(unsigned(a.batch) * a.n_q, unsigned((a.H + kCombHeads - 1) / kCombHeads));
+  if (a.act_dtype == MLA_FP32)
+    hipLaunchKernelGGL(combine_kernel<MLA_FP32>, grid, dim3(kCombNT), 0, st, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<MLA_BF16>, grid, dim3(kCombNT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

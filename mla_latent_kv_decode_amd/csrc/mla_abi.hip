@@ -1,0 +1,258 @@
+// Host side of the C ABI: argument validation, error reporting, kernel choice.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MLA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(int dt) { return dt == MLA_FP32 ? 4 : dt == MLA_BF16 ? 2 : 1; }
+
+// Checks shared by every call.  Returns MLA_OK or an error code.
+int check_dims(const mla_dims* d, bool need_cache_dtype) {
+  if (!d) return fail(MLA_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->num_heads < 1 || d->d_latent < 1 || d->d_rope < 0 || d->d_nope < 0 || d->d_v < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "bad dims: num_heads=%d d_latent=%d d_rope=%d d_nope=%d d_v=%d", d->num_heads,
+                d->d_latent, d->d_rope, d->d_nope, d->d_v);
+  if (d->d_rope % 2) return fail(MLA_ERR_INVALID_ARGUMENT, "d_rope=%d must be even", d->d_rope);
+  if (d->block_size < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "block_size=%d", d->block_size);
+  if (d->act_dtype != MLA_FP32 && d->act_dtype != MLA_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "act_dtype=%d must be MLA_FP32 or MLA_BF16", d->act_dtype);
+  if (need_cache_dtype && (d->cache_dtype < MLA_FP32 || d->cache_dtype > MLA_FP8_E4M3))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_dtype=%d", d->cache_dtype);
+  if (d->softmax_scale <= 0.f && d->d_nope + d->d_rope <= 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "default softmax scale needs d_nope + d_rope > 0");
+  return MLA_OK;
+}
+
+float eff_scale(const mla_dims* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale
+                                : float(1.0 / std::sqrt(double(d->d_nope + d->d_rope)));
+}
+
+int default_partitions(int n_q) {
+  int cu = mla_device_cu_count();
+  if (cu <= 0) cu = 256;
+  int g = cu / (n_q > 0 ? n_q : 1);
+  return g < 1 ? 1 : g;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t o_bytes, lse_off, total;
+};
+
+WsLayout ws_layout(const mla_dims* d, int batch, int n_q, int G) {
+  const size_t slots = mla::ws_slots(batch, G);
+  WsLayout w;
+  w.o_bytes = slots * size_t(n_q) * d->num_heads * d->d_latent * sizeof(float);
+  w.lse_off = align_up(w.o_bytes, 256);
+  w.total = align_up(w.lse_off + slots * size_t(n_q) * d->num_heads * sizeof(float), 256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+int mla_device_cu_count(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t d_model,
+                     const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
+                     const int32_t* positions, const int32_t* page_table,
+                     int32_t max_blocks_per_seq, void* cache, float* cache_scales,
+                     mla_stream_t stream) {
+  if (int e = check_dims(d, true)) return e;
+  if (n_tokens < 0 || d_model < 1 || max_blocks_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "n_tokens=%d d_model=%d max_blocks_per_seq=%d", n_tokens,
+                d_model, max_blocks_per_seq);
+  if (n_tokens == 0) return ok();
+  if (!h || !w_dkv || !seq_ids || !positions || !page_table || !cache || (d->d_rope > 0 && !w_kr))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if ((d->cache_dtype == MLA_FP8_E4M3) != (cache_scales != nullptr))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_scales must be given exactly for the fp8 cache");
+  const size_t ae = elem_bytes(d->act_dtype), ce = elem_bytes(d->cache_dtype);
+  if (!aligned(h, ae) || !aligned(w_dkv, ae) || (w_kr && !aligned(w_kr, ae)) || !aligned(cache, ce) ||
+      !aligned(seq_ids, 4) || !aligned(positions, 4) || !aligned(page_table, 4) ||
+      (cache_scales && !aligned(cache_scales, 4)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  mla::AppendArgs a;
+  a.h = h;
+  a.w_dkv = w_dkv;
+  a.w_kr = w_kr;
+  a.seq_ids = seq_ids;
+  a.positions = positions;
+  a.page_table = page_table;
+  a.cache = cache;
+  a.scales = cache_scales;
+  a.n_tokens = n_tokens;
+  a.d_model = d_model;
+  a.d_latent = d->d_latent;
+  a.d_rope = d->d_rope;
+  a.D = d->d_latent + d->d_rope;
+  a.block_size = d->block_size;
+  a.max_blocks = max_blocks_per_seq;
+  a.cache_dtype = d->cache_dtype;
+  a.act_dtype = d->act_dtype;
+  a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  if (!mla::append_supported(a))
+    return fail(MLA_ERR_UNSUPPORTED, "append: the RoPE part must lie in one 128-channel tile");
+  hipError_t e = mla::launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+size_t mla_decode_workspace_size(const mla_dims* d, int32_t batch, int32_t n_q,
+                                 int32_t num_partitions) {
+  if (!d || batch < 0 || n_q < 1 || d->num_heads < 1 || d->d_latent < 1) return 0;
+  const int G = num_partitions > 0 ? num_partitions : default_partitions(n_q);
+  return ws_layout(d, batch, n_q, G).total;
+}
+
+int mla_decode(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, const void* cache,
+               const float* cache_scales, const int32_t* page_table, int32_t max_blocks_per_seq,
+               const int32_t* seq_lens, int32_t num_partitions, void* workspace,
+               size_t workspace_bytes, mla_stream_t stream) {
+  if (int e = check_dims(d, true)) return e;
+  if (batch < 0 || n_q < 1 || max_blocks_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d max_blocks_per_seq=%d", batch, n_q,
+                max_blocks_per_seq);
+  if (batch == 0) return ok();
+  if (!q || !cache || !page_table || !seq_lens || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if ((d->cache_dtype == MLA_FP8_E4M3) != (cache_scales != nullptr))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_scales must be given exactly for the fp8 cache");
+  const size_t ae = elem_bytes(d->act_dtype), ce = elem_bytes(d->cache_dtype);
+  if (!aligned(q, ae) || !aligned(cache, ce) || !aligned(page_table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(workspace, 256))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer (workspace needs 256-byte alignment)");
+  const int G = num_partitions > 0 ? num_partitions : default_partitions(n_q);
+  const WsLayout w = ws_layout(d, batch, n_q, G);
+  if (workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes,
+                w.total);
+  mla::DecodeArgs a;
+  a.q = q;
+  a.cache = cache;
+  a.scales = cache_scales;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.lse_off);
+  a.batch = batch;
+  a.n_q = n_q;
+  a.H = d->num_heads;
+  a.D = d->d_latent + d->d_rope;
+  a.d_latent = d->d_latent;
+  a.block_size = d->block_size;
+  a.max_blocks = max_blocks_per_seq;
+  a.G = G;
+  a.cache_dtype = d->cache_dtype;
+  a.act_dtype = d->act_dtype;
+  a.scale = eff_scale(d);
+  hipError_t e;
+  if (!(d->flags & MLA_FLAG_GENERIC_DECODE) && mla::decode_mfma_supported(a)) {
+    e = mla::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
+  } else {
+    if (!mla::decode_generic_supported(a))
+      return fail(MLA_ERR_UNSUPPORTED, "decode: d_latent + d_rope = %d exceeds 1024", a.D);
+    e = mla::launch_decode_generic(a, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int mla_decode_combine(const mla_dims* d, const void* workspace, size_t workspace_bytes,
+                       int32_t batch, int32_t n_q, const int32_t* seq_lens, int32_t num_partitions,
+                       void* u_out, float* lse_out, mla_stream_t stream) {
+  if (int e = check_dims(d, false)) return e;
+  if (batch < 0 || n_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d", batch, n_q);
+  if (batch == 0) return ok();
+  if (!workspace || !seq_lens || !u_out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(workspace, 256) || !aligned(u_out, elem_bytes(d->act_dtype)) || !aligned(seq_lens, 4) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  const int G = num_partitions > 0 ? num_partitions : default_partitions(n_q);
+  const WsLayout w = ws_layout(d, batch, n_q, G);
+  if (workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes,
+                w.total);
+  mla::CombineArgs a;
+  a.ws_o = static_cast<const float*>(workspace);
+  a.ws_lse = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.lse_off);
+  a.seq_lens = seq_lens;
+  a.u = u_out;
+  a.lse_out = lse_out;
+  a.batch = batch;
+  a.n_q = n_q;
+  a.H = d->num_heads;
+  a.d_latent = d->d_latent;
+  a.block_size = d->block_size;
+  a.G = G;
+  a.act_dtype = d->act_dtype;
+  hipError_t e = mla::launch_combine(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+int mla_out_proj(const mla_dims* d, const void* u, int32_t rows, const void* w_uv, void* out,
+                 mla_stream_t stream) {
+  if (int e = check_dims(d, false)) return e;
+  if (rows < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "rows=%d", rows);
+  if (rows == 0) return ok();
+  if (!u || !w_uv || !out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t ae = elem_bytes(d->act_dtype);
+  if (!aligned(u, ae) || !aligned(w_uv, ae) || !aligned(out, ae))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  mla::OutProjArgs a;
+  a.u = u;
+  a.w = w_uv;
+  a.out = out;
+  a.rows = rows;
+  a.H = d->num_heads;
+  a.d_latent = d->d_latent;
+  a.d_v = d->d_v;
+  a.act_dtype = d->act_dtype;
+  hipError_t e = mla::launch_out_proj(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "out_proj launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal kernel-argument structs and launchers of the MLA decode library.
+#pragma once
+
+#include "mla_common.h"
+
+namespace mla {
+
+struct DecodeArgs {
+  const void* q;           // [B][n_q][H][D] act dtype
+  const void* cache;       // [nblk][bs][D]
+  const float* scales;     // [nblk][bs][ntiles] (fp8) or null
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float* ws_o;             // [slots][n_q][H][d_latent]
+  float* ws_lse;           // [slots][n_q][H]
+  int batch, n_q, H, D, d_latent, block_size, max_blocks, G;
+  int cache_dtype, act_dtype;
+  float scale;
+};
+
+struct CombineArgs {
+  const float* ws_o;
+  const float* ws_lse;
+  const int32_t* seq_lens;
+  void* u;                 // [B][n_q][H][d_latent] act dtype
+  float* lse_out;          // [B][n_q][H] or null
+  int batch, n_q, H, d_latent, block_size, G;
+  int act_dtype;
+};
+
+struct AppendArgs {
+  const void* h;           // [T][d_model]
+  const void* w_dkv;       // [d_latent][d_model]
+  const void* w_kr;        // [d_rope][d_model]
+  const int32_t* seq_ids;
+  const int32_t* positions;
+  const int32_t* page_table;
+  void* cache;
+  float* scales;
+  int n_tokens, d_model, d_latent, d_rope, D, block_size, max_blocks;
+  int cache_dtype, act_dtype;
+  float rope_base;
+};
+
+struct OutProjArgs {
+  const void* u;           // [rows][H][d_latent]
+  const void* w;           // [H][d_v][d_latent]
+  void* out;               // [rows][H][d_v]
+  int rows, H, d_latent, d_v;
+  int act_dtype;
+};
+
+bool decode_generic_supported(const DecodeArgs& a);
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
+bool decode_mfma_supported(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+bool append_supported(const AppendArgs& a);
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,145 @@
+"""Shared builders for GPU parity tests: seeded inputs on the device plus the
+oracle's view of the same bytes.  Expected values come only from ``oracle/``."""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+import mla_workloads as W
+from oracle import mla_oracle as O
+
+DT = {"fp32": 0, "bf16": 1, "fp8": 2}
+TORCH_ACT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def dims_of(cfg: W.Config, flags: int = 0, act: Optional[str] = None):
+    import mla_latent_kv_decode_amd as M
+    d = cfg.dims
+    return M.make_dims(d.num_heads, d.d_latent, d.d_rope, d.d_nope, d.d_v, d.block_size,
+                       DT[cfg.cache_dtype], DT[act or cfg.act_dtype], flags=flags)
+
+
+def rel_l2(x, y) -> float:
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    return float(np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300))
+
+
+def max_abs(x, y) -> float:
+    return float(np.max(np.abs(np.asarray(x, np.float64) - np.asarray(y, np.float64))))
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 view of a device tensor (fp32 / bf16)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+    return t.to(torch.float64).numpy()
+
+
+class DecodeCase:
+    """A paged-cache decode problem resident on the GPU.
+
+    Tail slots past each sequence's length and the guard blocks (never
+    referenced) hold NaN, so an out-of-range read shows up in the outputs.
+    """
+
+    def __init__(self, cfg: W.Config, device="cuda", guard: int = 2, nan_tail: bool = True,
+                 act: Optional[str] = None, shuffle: bool = True, table=None, lens=None):
+        self.cfg = cfg
+        d = self.d = cfg.dims
+        self.act = act or cfg.act_dtype
+        self.lens = W.seq_lens(cfg) if lens is None else np.asarray(lens, np.int32)
+        if table is None:
+            self.table, self.nblk = W.page_table(self.lens, d.block_size, cfg.seed, shuffle, guard)
+        else:
+            self.table, self.nblk = table
+        bs, D = d.block_size, d.row
+        rows = W.cache_rows(self.nblk * bs, cfg, seed=cfg.seed + 10, device=device)
+        self.scales = None
+        if cfg.cache_dtype == "fp32":
+            pool = rows.view(self.nblk, bs, D).clone()
+        elif cfg.cache_dtype == "bf16":
+            pool = rows.to(torch.bfloat16).view(self.nblk, bs, D)
+        else:
+            codes, scales = O.quantize_fp8_rows(rows.cpu().numpy())
+            pool = torch.from_numpy(codes).to(device).view(self.nblk, bs, D)
+            self.scales = torch.from_numpy(scales).to(device).view(self.nblk, bs, -1)
+        del rows
+        used = np.zeros((self.nblk, bs), bool)
+        for b, L in enumerate(self.lens):
+            nb = (int(L) + bs - 1) // bs
+            blk = self.table[b, :nb]
+            flat = np.zeros(nb * bs, bool)
+            flat[:L] = True
+            used[blk] = flat.reshape(nb, bs)
+        if nan_tail:
+            mask = torch.from_numpy(~used).to(device)
+            if cfg.cache_dtype == "fp8":
+                pool[mask] = 0x7F
+                self.scales[mask] = float("nan")
+            else:
+                pool[mask] = float("nan")
+        self.pool = pool
+        self.q = W.absorbed_queries(cfg, seed=cfg.seed + 20, device=device).to(TORCH_ACT[self.act])
+        self.table_t = torch.from_numpy(self.table).to(device)
+        self.lens_t = torch.from_numpy(self.lens).to(device)
+        self.scale = O.softmax_scale(d.d_nope, d.d_rope)
+
+    # -- oracle side -----------------------------------------------------
+    def oracle_rows(self, b: int) -> np.ndarray:
+        d = self.d
+        L = int(self.lens[b])
+        nb = (L + d.block_size - 1) // d.block_size
+        idx = torch.from_numpy(self.table[b, :nb].astype(np.int64)).to(self.pool.device)
+        blocks = self.pool.index_select(0, idx).cpu()
+        if self.cfg.cache_dtype == "fp8":
+            sc = self.scales.index_select(0, idx).cpu().numpy()
+            vals = O.dequantize_fp8_rows(blocks.numpy(), sc)
+        else:
+            vals = to_f64(blocks)
+        return vals.reshape(nb * d.block_size, d.row)[:L]
+
+    def oracle(self, b: int):
+        qb = to_f64(self.q[b])
+        return O.attend_absorbed(qb, self.oracle_rows(b), self.cfg.n_q, self.d.d_latent, self.scale)
+
+    # -- GPU side ----------------------------------------------------------
+    def run(self, flags: int = 0, G: int = 0):
+        import mla_latent_kv_decode_amd as M
+        dims = dims_of(self.cfg, flags, self.act)
+        B, n_q = self.q.shape[0], self.q.shape[1]
+        ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, G), dtype=torch.uint8,
+                         device=self.q.device)
+        M.mla_decode(dims, self.q, self.pool, self.scales, self.table_t, self.lens_t, ws, G)
+        u = torch.empty(B, n_q, self.d.num_heads, self.d.d_latent, dtype=TORCH_ACT[self.act],
+                        device=self.q.device)
+        lse = torch.empty(B, n_q, self.d.num_heads, dtype=torch.float32, device=self.q.device)
+        M.mla_decode_combine(dims, ws, self.lens_t, u, lse, G)
+        torch.cuda.synchronize()
+        return u, lse
+
+
+def compare_sampled(case: DecodeCase, u, lse, batch_ids: List[int], rel_bar=1e-2, abs_bar=2e-2,
+                    lse_tol=1e-3) -> Dict[str, float]:
+    """Compare GPU outputs with the oracle on the listed sequences; returns metrics."""
+    got, want, gl, wl = [], [], [], []
+    for b in batch_ids:
+        ou, ol = case.oracle(b)
+        got.append(to_f64(u[b]))
+        want.append(ou)
+        gl.append(lse[b].cpu().numpy().astype(np.float64))
+        wl.append(ol)
+    got, want = np.stack(got), np.stack(want)
+    m = {"rel_l2": rel_l2(got, want), "max_abs": max_abs(got, want),
+         "lse_max_abs": max_abs(np.stack(gl), np.stack(wl)),
+         "worst_seq_rel_l2": max(rel_l2(g, w) for g, w in zip(got, want))}
+    assert np.all(np.isfinite(got)), "non-finite output (a masked or guard row leaked?)"
+    assert m["rel_l2"] <= rel_bar, m
+    if abs_bar is not None:
+        assert m["max_abs"] <= abs_bar, m
+    assert m["lse_max_abs"] <= lse_tol, m
+    return m

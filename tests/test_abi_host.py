@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+declared in include/mla.h, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mla_latent_kv_decode_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from mla_latent_kv_decode_amd import build
+        build.build()
+    return _lib
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_hot_path_calls():
+    names = declared_functions()
+    for n in ["mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(declared_functions()) == set(L.EXPORTS)
+    assert L.mla_abi_version() == 1
+
+
+def _dims(L, **kw):
+    base = dict(num_heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128, block_size=64,
+                cache_dtype=L.BF16, act_dtype=L.BF16)
+    base.update(kw)
+    return L.make_dims(**base)
+
+
+FAKE = 1 << 20  # aligned, non-null, never dereferenced: validation fails first
+
+
+def test_decode_validation_errors(L):
+    lib = L.lib()
+    d = _dims(L)
+    ws = L.mla_decode_workspace_size(d, 4, 1, 8)
+    assert ws > 0
+    call = lambda dims, q=FAKE, batch=4, n_q=1, ws_bytes=ws, seq=FAKE, sc=None, G=8: lib.mla_decode(
+        dims, q, batch, n_q, FAKE, sc, FAKE, 16, seq, G, FAKE, ws_bytes, None)
+    assert call(None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), n_q=0) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), q=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), seq=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), q=FAKE + 1) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), ws_bytes=ws - 1) == L.ERR_WORKSPACE_TOO_SMALL
+    assert "workspace" in lib.mla_last_error().decode()
+    assert call(ctypes.byref(d), sc=FAKE) == L.ERR_INVALID_ARGUMENT   # scales for a bf16 cache
+    d8 = _dims(L, cache_dtype=L.FP8_E4M3)
+    assert call(ctypes.byref(d8)) == L.ERR_INVALID_ARGUMENT            # fp8 without scales
+    bad = _dims(L, d_rope=63)
+    assert call(ctypes.byref(bad)) == L.ERR_INVALID_ARGUMENT
+    bad = _dims(L, act_dtype=L.FP8_E4M3)
+    assert call(ctypes.byref(bad)) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), batch=0) == L.OK                       # nothing to do
+    big = _dims(L, d_latent=1024, flags=L.FLAG_GENERIC_DECODE)
+    ws_big = L.mla_decode_workspace_size(big, 4, 1, 8)
+    assert lib.mla_decode(ctypes.byref(big), FAKE, 4, 1, FAKE, None, FAKE, 16, FAKE, 8, FAKE,
+                          ws_big, None) == L.ERR_UNSUPPORTED
+
+
+def test_workspace_size_closed_form(L):
+    d = _dims(L)
+    B, n_q, G, H, dc = 64, 1, 256, 128, 512
+    slots = B + G
+    o = slots * n_q * H * dc * 4
+    lse = slots * n_q * H * 4
+    want = (((o + 255) // 256 * 256 + lse) + 255) // 256 * 256
+    assert L.mla_decode_workspace_size(d, B, n_q, G) == want
+    assert L.mla_decode_workspace_size(d, B, 0, G) == 0
+
+
+def test_other_entry_points_validate(L):
+    lib = L.lib()
+    d = _dims(L)
+    assert lib.mla_decode_combine(ctypes.byref(d), FAKE, 10, 4, 1, FAKE, 8, FAKE, None, None) \
+        == L.ERR_WORKSPACE_TOO_SMALL
+    assert lib.mla_decode_combine(ctypes.byref(d), None, 10, 4, 1, FAKE, 8, FAKE, None, None) \
+        == L.ERR_INVALID_ARGUMENT
+    assert lib.mla_out_proj(ctypes.byref(d), FAKE, -1, FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT
+    assert lib.mla_out_proj(ctypes.byref(d), None, 4, FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT
+    assert lib.mla_out_proj(ctypes.byref(d), FAKE, 0, FAKE, FAKE, None) == L.OK
+    assert lib.mla_cache_append(ctypes.byref(d), FAKE, 4, 7168, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT  # scales on bf16
+    straddle = _dims(L, d_latent=100)
+    assert lib.mla_cache_append(ctypes.byref(straddle), FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                16, FAKE, None, None) == L.ERR_UNSUPPORTED
+    assert lib.mla_cache_append(ctypes.byref(d), FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                FAKE, None, None) == L.OK

@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (from the stated tolerances of the method): bf16 inputs with fp32
+accumulation -> relative L2 <= 1e-2 and max-abs <= 2e-2; fp8-e4m3 caches ->
+relative L2 <= 5e-2; fp32 workloads are additionally held to 1e-5 relative L2.
+Index and placement work (page tables, slots) is checked bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_workloads as W
+from oracle import mla_oracle as O
+from tests.cases import DT, DecodeCase, compare_sampled, dims_of, max_abs, rel_l2, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_decode_amd as M
+    M.lib()  # raises if the HIP library is missing: no fallback exists
+    return M
+
+
+def _t(x, dtype, dev="cuda"):
+    return torch.as_tensor(np.asarray(x)).to(dev).to(dtype)
+
+
+# --------------------------------------------------------------------------
+# tiny fp32 workload, end to end: append -> decode -> combine -> out_proj
+# --------------------------------------------------------------------------
+def test_tiny_end_to_end_fp32():
+    import mla_latent_kv_decode_amd as M
+    cfg = W.CONFIGS["tiny"]
+    d = cfg.dims
+    dm, H = d.d_model, d.num_heads
+    w_dkv = W.weight(d.d_latent, dm, 1).numpy()
+    w_kr = W.weight(d.d_rope, dm, 2).numpy()
+    w_q = W.weight(H * (d.d_nope + d.d_rope), dm, 3).numpy()
+    w_uk = W.normal((H, d.d_nope, d.d_latent), 4, std=1 / math.sqrt(d.d_latent)).numpy()
+    w_uv = W.normal((H, d.d_v, d.d_latent), 5, std=1 / math.sqrt(d.d_latent)).numpy()
+    h = W.normal((65, dm), 6).numpy()          # positions 0..63 prior, 64 = query token
+    pos = np.arange(65, dtype=np.int32)
+    # oracle
+    rows = O.kv_rows(h, w_dkv, w_kr, pos)
+    q, _, _ = O.query_from_hidden(h[64], w_q, w_uk, 64, H, d.d_nope, d.d_rope)
+    scale = O.softmax_scale(d.d_nope, d.d_rope)
+    u_ref, lse_ref = O.attend_absorbed(q[None], rows, 1, d.d_latent, scale)
+    o_ref = O.out_proj(u_ref, w_uv)
+    # GPU: contiguous cache = identity page table over 2 blocks of 64
+    dims = dims_of(cfg)
+    cache = torch.full((2, 64, d.row), float("nan"), device="cuda")
+    table = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+    M.mla_cache_append(dims, _t(h, torch.float32), _t(w_dkv, torch.float32),
+                       _t(w_kr, torch.float32), torch.zeros(65, dtype=torch.int32, device="cuda"),
+                       _t(pos, torch.int32), table, cache)
+    lens = torch.tensor([65], dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.mla_decode_workspace_size(dims, 1, 1, 0), dtype=torch.uint8, device="cuda")
+    qd = _t(q, torch.float32).view(1, 1, H, d.row)
+    M.mla_decode(dims, qd, cache, None, table, lens, ws)
+    u = torch.empty(1, 1, H, d.d_latent, device="cuda")
+    lse = torch.empty(1, 1, H, device="cuda")
+    M.mla_decode_combine(dims, ws, lens, u, lse)
+    o = torch.empty(1, H, d.d_v, device="cuda")
+    M.mla_out_proj(dims, u.view(1, H, d.d_latent), _t(w_uv, torch.float32), o)
+    torch.cuda.synchronize()
+    got_rows = cache.view(-1, d.row)[:65].cpu().numpy().astype(np.float64)
+    assert rel_l2(got_rows, rows) <= 1e-6
+    assert rel_l2(u.cpu().numpy()[0], u_ref) <= 1e-5
+    assert max_abs(lse.cpu().numpy()[0], lse_ref) <= 1e-5
+    assert rel_l2(o.cpu().numpy(), o_ref) <= 1e-5
+    assert max_abs(o.cpu().numpy(), o_ref) <= 2e-2
+    assert torch.isnan(cache.view(-1, d.row)[65:]).all(), "slots past the sequence were written"
+
+
+# --------------------------------------------------------------------------
+# append: placement is bit-exact (identity projection), values match the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cache_dtype", ["fp32", "bf16", "fp8"])
+def test_append_identity_projection_bit_exact(cache_dtype):
+    import mla_latent_kv_decode_amd as M
+    d_c, d_r, bs = 512, 64, 64
+    D = d_c + d_r
+    act = "fp32" if cache_dtype == "fp32" else "bf16"
+    tdt = torch.float32 if act == "fp32" else torch.bfloat16
+    rng = np.random.default_rng(7)
+    lens = np.array([130, 64, 300], np.int32)
+    table, nblk = W.page_table(lens, bs, seed=7, guard_blocks=2)
+    # 40 tokens at distinct positions; several at position 0
+    toks = []
+    for b, L in enumerate(lens):
+        for p in rng.choice(L, size=13 + b, replace=False):
+            toks.append((b, int(p)))
+    toks += [(0, 0), (2, 0)]
+    toks = list(dict.fromkeys(toks))
+    seq_ids = np.array([t[0] for t in toks], np.int32)
+    positions = np.array([t[1] for t in toks], np.int32)
+    T = len(toks)
+    h = W.normal((T, D), 8).to(tdt)
+    h64 = to_f64(h)
+    w_dkv = np.concatenate([np.eye(d_c), np.zeros((d_c, d_r))], 1)
+    w_kr = np.concatenate([np.zeros((d_r, d_c)), np.eye(d_r)], 1)
+    cfg = W.Config("ident", W.Dims(1, d_c, d_r, 128, 128, D), 3, 1, 0, cache_dtype, act, None)
+    dims = dims_of(cfg)
+    if cache_dtype == "fp8":
+        cache = torch.full((nblk, bs, D), 0x7F, dtype=torch.uint8, device="cuda")
+        scales = torch.full((nblk, bs, 5), float("nan"), device="cuda")
+    else:
+        cache = torch.full((nblk, bs, D), float("nan"), dtype=tdt, device="cuda")
+        scales = None
+    before = cache.clone()
+    M.mla_cache_append(dims, h.cuda(), _t(w_dkv, tdt), _t(w_kr, tdt), _t(seq_ids, torch.int32),
+                       _t(positions, torch.int32), _t(table, torch.int32), cache, scales)
+    torch.cuda.synchronize()
+    pool = {"dtype": cache_dtype, "data": None}
+    written = np.zeros((nblk, bs), bool)
+    for i in range(T):
+        blk, off = O.slot_of(table, int(seq_ids[i]), int(positions[i]), bs)
+        written[blk, off] = True
+        want = O.kv_rows(h64[i:i + 1], w_dkv, w_kr, positions[i:i + 1])[0].astype(np.float32)
+        if cache_dtype == "fp8":
+            codes, sc = O.quantize_fp8_row(want)
+            got_c = cache[blk, off].cpu().numpy()
+            got_s = scales[blk, off].cpu().numpy()
+            # latent tiles: exact inputs -> the same fp32 decisions -> identical bytes
+            assert np.array_equal(got_c[:d_c], codes[:d_c]), (i, positions[i])
+            assert np.array_equal(got_s[:4], sc[:4])
+            if positions[i] == 0:
+                assert np.array_equal(got_c, codes) and np.array_equal(got_s, sc)
+            dec = O.dequantize_fp8_rows(got_c[None], got_s[None])[0]
+            assert rel_l2(dec[d_c:], want[d_c:]) <= 5e-2
+        else:
+            got = to_f64(cache[blk, off])
+            assert np.array_equal(got[:d_c], h64[i, :d_c]), "latent part must be copied exactly"
+            if positions[i] == 0:
+                assert np.array_equal(got, h64[i]), "RoPE at position 0 is the identity"
+            # rotated part: fp32 rotation on the device vs float64 here
+            if cache_dtype == "fp32":
+                bound = 1e-6 * np.maximum(np.abs(want[d_c:]), 1.0)
+            else:
+                bound = 2.0 ** -8 * np.maximum(np.abs(want[d_c:]), 0.01)
+            assert np.all(np.abs(got[d_c:] - want[d_c:]) <= bound)
+    untouched = torch.from_numpy(~written).cuda()
+    a, b = cache[untouched], before[untouched]
+    if cache_dtype == "fp8":
+        assert torch.equal(a, b)
+        assert torch.isnan(scales[untouched]).all()
+    else:
+        assert torch.equal(a.view(torch.int16 if act == "bf16" else torch.int32),
+                           b.view(torch.int16 if act == "bf16" else torch.int32))
+
+
+def test_append_v3_random_weights_bf16():
+    import mla_latent_kv_decode_amd as M
+    d = W.V3
+    T = 64
+    h = W.normal((T, d.d_model), 11).to(torch.bfloat16)
+    w_dkv = W.weight(d.d_latent, d.d_model, 12, dtype=torch.bfloat16)
+    w_kr = W.weight(d.d_rope, d.d_model, 13, dtype=torch.bfloat16)
+    lens = np.full(T, 4096, np.int32)
+    table, nblk = W.page_table(lens, 64, seed=5)
+    positions = np.full(T, 4095, np.int32)
+    seq_ids = np.arange(T, dtype=np.int32)
+    cfg = W.CONFIGS["v3"]
+    dims = dims_of(cfg)
+    cache = torch.zeros((nblk, 64, d.row), dtype=torch.bfloat16, device="cuda")
+    M.mla_cache_append(dims, h.cuda(), w_dkv.cuda(), w_kr.cuda(), _t(seq_ids, torch.int32),
+                       _t(positions, torch.int32), _t(table, torch.int32), cache)
+    torch.cuda.synchronize()
+    want = O.kv_rows(to_f64(h), to_f64(w_dkv), to_f64(w_kr), positions)
+    got = np.stack([to_f64(cache[table[b, 63], 63]) for b in range(T)])
+    assert rel_l2(got, want) <= 4e-3
+    assert max_abs(got, want) <= 2e-2
+
+
+# --------------------------------------------------------------------------
+# decode + combine
+# --------------------------------------------------------------------------
+SMALL = [
+    ("bf16", 1, W.scaled(W.CONFIGS["v3"], batch=3, seq_len=333)),
+    ("bf16", 2, W.scaled(W.CONFIGS["ragged"], batch=5, len_lo=2, len_hi=400)),
+    ("fp8", 1, W.scaled(W.CONFIGS["fp8"], batch=3, seq_len=200)),
+]
+
+
+@pytest.mark.parametrize("G", [1, 5, 37])
+@pytest.mark.parametrize("idx", range(len(SMALL)))
+def test_decode_generic_small(idx, G):
+    import mla_latent_kv_decode_amd as M
+    _, _, cfg = SMALL[idx]
+    case = DecodeCase(cfg)
+    u, lse = case.run(flags=M.FLAG_GENERIC_DECODE, G=G)
+    # fp8 caches are held to relative L2 only (the stated fp8 tolerance)
+    fp8 = cfg.cache_dtype == "fp8"
+    compare_sampled(case, u, lse, list(range(cfg.batch)), rel_bar=5e-2 if fp8 else 1e-2,
+                    abs_bar=None if fp8 else 2e-2)
+
+
+def test_decode_fp32_tight_and_partition_invariance():
+    """fp32 queries and outputs over a bf16 cache: every partition count gives
+    the oracle's result to fp32 accuracy (the LSE merge is exact up to rounding)."""
+    import mla_latent_kv_decode_amd as M
+    cfg = W.scaled(W.CONFIGS["ragged"], batch=4, len_lo=1, len_hi=700)
+    case = DecodeCase(cfg, act="fp32")
+    outs = []
+    for G in [1, 3, 16, 200]:
+        u, lse = case.run(flags=M.FLAG_GENERIC_DECODE, G=G)
+        compare_sampled(case, u, lse, list(range(cfg.batch)), rel_bar=1e-5, abs_bar=1e-4,
+                        lse_tol=1e-4)
+        outs.append(u.cpu().numpy())
+    for o in outs[1:]:
+        assert rel_l2(o, outs[0]) <= 1e-6
+
+
+def test_decode_page_table_permutation_is_bitwise_invariant():
+    import mla_latent_kv_decode_amd as M
+    cfg = W.scaled(W.CONFIGS["v3"], batch=2, seq_len=500)
+    a = DecodeCase(cfg, shuffle=False, guard=0)
+    # same logical rows, physical blocks permuted
+    perm = np.random.default_rng(3).permutation(a.nblk)
+    b_table = perm[a.table].astype(np.int32)
+    b = DecodeCase(cfg, table=(b_table, a.nblk), guard=0)
+    inv = torch.from_numpy(np.argsort(perm)).cuda()
+    b.pool = a.pool.clone()
+    b.pool[torch.from_numpy(perm).cuda()] = a.pool
+    ua, la = a.run(G=7)
+    ub, lb = b.run(G=7)
+    assert torch.equal(ua.view(torch.int16), ub.view(torch.int16))
+    assert torch.equal(la, lb)
+
+
+def test_out_proj_v3_bf16():
+    import mla_latent_kv_decode_amd as M
+    d = W.V3
+    rows = 70
+    u = W.normal((rows, d.num_heads, d.d_latent), 21).to(torch.bfloat16)
+    w = W.normal((d.num_heads, d.d_v, d.d_latent), 22, std=1 / math.sqrt(d.d_latent)).to(torch.bfloat16)
+    out = torch.empty(rows, d.num_heads, d.d_v, dtype=torch.bfloat16, device="cuda")
+    M.mla_out_proj(dims_of(W.CONFIGS["v3"]), u.cuda(), w.cuda(), out)
+    torch.cuda.synchronize()
+    ref = O.out_proj(to_f64(u), to_f64(w))
+    assert rel_l2(to_f64(out), ref) <= 4e-3
+    assert max_abs(to_f64(out), ref) <= 2e-2
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, default launch configuration, sampled sequences
+# --------------------------------------------------------------------------
+FULL = {"v3": [0, 17, 63], "long": [0, 3]}
+
+
+@pytest.mark.parametrize("name", sorted(FULL))
+def test_full_size_sampled(name):
+    cfg = W.CONFIGS[name]
+    case = DecodeCase(cfg)
+    u, lse = case.run()
+    compare_sampled(case, u, lse, FULL[name])
+    assert torch.isfinite(u.float()).all()
