@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA decode step over a paged latent cache on one MI355X.
+
+A step is one pass of the whole hot path on one batch of synthetic input:
+  mla_cache_append  (B new tokens: W^DKV / W^KR projection, RoPE, paged write)
+  mla_decode        (split-KV attention over the latent cache, all heads)
+  mla_decode_combine(log-sum-exp merge of the splits)
+  mla_out_proj      (per-head W^UV up-projection)
+Default workload: DeepSeek-V3 shape, bf16, B=64 sequences of L=4096 cached
+tokens, one query token each, H=128, d_c=512, d_R=64, block 64, shuffled page
+table.  Inputs are resident in HBM before timing; several copies of the pool
+are rotated so the 256 MB last-level cache cannot serve the cache stream.
+
+Prints one JSON line (rank 0).  Metric: KV-tokens/s = sum_b L_b per step / time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+BYTES_PER_KV_TOKEN = {"bf16": 1152, "fp8": 596, "fp32": 2304}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="v3", choices=["v3", "long", "ragged", "fp8"])
+    p.add_argument("--partitions", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--generic", action="store_true", help="force the generic decode kernel")
+    return p.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mla_latent_kv_decode_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash(kernel_src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs the whole hot path on a single "
+              f"MI355X (no sharding, no collectives); got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_workloads as W
+    import mla_latent_kv_decode_amd as M
+
+    M.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.CONFIGS[args.workload]
+    d = cfg.dims
+    bs, D, H = d.block_size, d.row, d.num_heads
+    lens = W.seq_lens(cfg)
+    B, n_q = cfg.batch, cfg.n_q
+    table, nblk = W.page_table(lens, bs, cfg.seed)
+    kv_tokens = int(lens.sum())
+    cdt = {"bf16": M.BF16, "fp8": M.FP8_E4M3}[cfg.cache_dtype]
+    dims = M.make_dims(H, d.d_latent, d.d_rope, d.d_nope, d.d_v, bs, cdt, M.BF16,
+                       flags=M.FLAG_GENERIC_DECODE if args.generic else 0)
+
+    # ---- resident inputs -------------------------------------------------
+    elem = 1 if cfg.cache_dtype == "fp8" else 2
+    pool_bytes = nblk * bs * D * elem
+    n_copies = max(2, math.ceil(1.0e9 / pool_bytes) + 1)
+    pools, scales = [], []
+    for i in range(n_copies):
+        rows = W.cache_rows(nblk * bs, cfg, seed=cfg.seed + 10 + i, device=dev)
+        if cfg.cache_dtype == "fp8":
+            # synthetic e4m3 bytes: the workload's rows reduced to codes by the
+            # library's own cast; the benchmark times decode, not the codec
+            amax = rows.view(-1, D)[:, :].abs().amax(dim=1, keepdim=True).clamp_min(1e-6)
+            sc = (amax / 448.0).expand(-1, 5).contiguous()
+            pools.append((rows / amax * 448.0).clamp(-448, 448).to(torch.float8_e4m3fn)
+                         .view(torch.uint8).view(nblk, bs, D))
+            scales.append(sc.view(nblk, bs, 5))
+        else:
+            pools.append(rows.to(torch.bfloat16).view(nblk, bs, D))
+            scales.append(None)
+        del rows
+    q = W.absorbed_queries(cfg, seed=cfg.seed + 20, device=dev).to(torch.bfloat16)
+    table_t = torch.from_numpy(table).to(dev)
+    lens_t = torch.from_numpy(lens).to(dev)
+    # append inputs: the n_q newest tokens of every sequence
+    T = B * n_q
+    h = W.normal((T, d.d_model), cfg.seed + 30, device=dev, dtype=torch.bfloat16)
+    w_dkv = W.weight(d.d_latent, d.d_model, cfg.seed + 31, dtype=torch.bfloat16, device=dev)
+    w_kr = W.weight(d.d_rope, d.d_model, cfg.seed + 32, dtype=torch.bfloat16, device=dev)
+    w_uv = W.normal((H, d.d_v, d.d_latent), cfg.seed + 33, std=1 / math.sqrt(d.d_latent),
+                    device=dev, dtype=torch.bfloat16)
+    seq_ids = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(n_q)
+    positions = (lens_t.repeat_interleave(n_q) - n_q
+                 + torch.arange(n_q, dtype=torch.int32, device=dev).repeat(B)).to(torch.int32)
+    G = args.partitions
+    ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, G), dtype=torch.uint8, device=dev)
+    u = torch.empty(B, n_q, H, d.d_latent, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(B * n_q, H, d.d_v, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        pool, sc = pools[i % n_copies], scales[i % n_copies]
+        if ev: ev[0].record(stream)
+        M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc)
+        if ev: ev[1].record(stream)
+        M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G)
+        if ev: ev[2].record(stream)
+        M.mla_decode_combine(dims, ws, lens_t, u, None, G)
+        if ev: ev[3].record(stream)
+        M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o)
+        if ev: ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ------------------------------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
+    k_ms = per.mean(axis=0)
+    decode_ms = float(k_ms[1])
+
+    # ---- roofline of the dominant kernel (decode) ---------------------------
+    bytes_alg = kv_tokens * BYTES_PER_KV_TOKEN[cfg.cache_dtype] + B * n_q * H * D * 2
+    flops_alg = kv_tokens * n_q * 2 * H * (D + d.d_latent)
+    achieved_gbps = bytes_alg / (decode_ms * 1e-3) / 1e9
+    achieved_tflops = flops_alg / (decode_ms * 1e-3) / 1e12
+    kernel_src = "decode_generic.hip" if args.generic else "decode_mfma.hip"
+    traffic = traffic_from_profile(kernel_src, args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": traffic,
+                "mfma_tflops": round(achieved_tflops, 1),
+                "mfma_frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "bytes_alg_per_launch": bytes_alg, "flops_alg_per_launch": flops_alg,
+                "kernel_ms": round(decode_ms, 5)}
+
+    # ---- CPU baseline: the oracle on a bounded sample ----------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, pools[0], scales[0], table, lens, q, h, w_dkv, w_kr, w_uv,
+                           args.cpu_seconds)
+
+    out = {
+        "metric": "MLA decode KV-tokens/s (+ achieved HBM GB/s and MFMA TFLOP/s vs roofline)",
+        "value": round(kv_tokens * args.steps / (total_ms * 1e-3), 1),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} L={'ragged' if cfg.seq_len is None else cfg.seq_len} "
+                               f"n_q={n_q} H={H} d_c={d.d_latent} d_R={d.d_rope} block={bs} "
+                               f"cache={cfg.cache_dtype}",
+                   "batch": B, "kv_tokens_per_step": kv_tokens, "n_q": n_q,
+                   "partitions": G, "pool_copies_rotated": n_copies},
+        "kernels_ms": {"append": round(float(k_ms[0]), 5), "decode": round(decode_ms, 5),
+                       "combine": round(float(k_ms[2]), 5), "out_proj": round(float(k_ms[3]), 5)},
+        "decode_kernel": "generic" if args.generic else "default",
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, pool, sc, table, lens, q, h, w_dkv, w_kr, w_uv, seconds):
+    """The oracle as it stands (float64 NumPy), on a bounded sample of the same
+    workload: the first few sequences' decode plus their append rows and
+    up-projection, repeated until about ``seconds`` of CPU work."""
+    import torch
+    from oracle import mla_oracle as O
+
+    d = cfg.dims
+    bs = d.block_size
+    n_seq = 4
+    ids = list(range(n_seq))
+    host_pool = {"dtype": cfg.cache_dtype}
+    blocks = np.unique(table[ids][table[ids] >= 0])
+    data = np.zeros((pool.shape[0],) + tuple(pool.shape[1:]),
+                    dtype=np.uint8 if cfg.cache_dtype == "fp8" else np.uint16)
+    idx = torch.from_numpy(blocks.astype(np.int64)).to(pool.device)
+    raw = pool.index_select(0, idx).cpu()
+    data[blocks] = raw.numpy() if cfg.cache_dtype == "fp8" else raw.view(torch.int16).numpy().view(np.uint16)
+    host_pool["data"] = data
+    if sc is not None:
+        s = np.zeros((pool.shape[0], bs, 5), np.float32)
+        s[blocks] = sc.index_select(0, idx).cpu().numpy()
+        host_pool["scales"] = s
+
+    def f64(t):
+        return O.bf16_bits_to_f64(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+
+    qh = f64(q[:n_seq])
+    hh = f64(h[:n_seq * cfg.n_q])
+    wd, wk, wu = f64(w_dkv), f64(w_kr), f64(w_uv)
+    scale = O.softmax_scale(d.d_nope, d.d_rope)
+    pos = (lens[:n_seq].repeat(cfg.n_q) - 1).astype(np.int64)
+    reps, t_start = 0, time.perf_counter()
+    while True:
+        O.kv_rows(hh, wd, wk, pos)
+        res = O.decode(qh, host_pool, table, lens, bs, d.d_latent, scale, batch_ids=ids)
+        O.out_proj(np.concatenate([res[b][0] for b in ids]), wu)
+        reps += 1
+        el = time.perf_counter() - t_start
+        if el >= seconds or reps >= 1000:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(reps * int(lens[:n_seq].sum()) / el, 1), "unit": "KV-tokens/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{n_seq} of {cfg.batch} sequences ({int(lens[:n_seq].sum())} KV-tokens), "
+                      f"append rows + absorbed decode + W^UV in float64 NumPy, {reps} repetitions "
+                      f"in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
