@@ -124,6 +124,8 @@ def main():
     seq_ids = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(n_q)
     positions = (lens_t.repeat_interleave(n_q) - n_q
                  + torch.arange(n_q, dtype=torch.int32, device=dev).repeat(B)).to(torch.int32)
+    aws_n = M.mla_cache_append_workspace_size(dims, T, d.d_model)
+    aws = torch.empty(aws_n, dtype=torch.uint8, device=dev) if aws_n else None
     G = args.partitions
     ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, G), dtype=torch.uint8, device=dev)
     u = torch.empty(B, n_q, H, d.d_latent, dtype=torch.bfloat16, device=dev)
@@ -133,7 +135,7 @@ def main():
     def step(i, ev=None):
         pool, sc = pools[i % n_copies], scales[i % n_copies]
         if ev: ev[0].record(stream)
-        M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc)
+        M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc, aws)
         if ev: ev[1].record(stream)
         M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G)
         if ev: ev[2].record(stream)

@@ -111,14 +111,21 @@ int mla_device_cu_count(void);
  * Accumulation is fp32; the row is stored in cache_dtype (bf16: RNE; fp8:
  * per-tile amax scaling, scale = amax/448, code = e4m3_rne_sat(x * (448/amax)),
  * scale 1 and zero codes for an all-zero tile).  Two tokens mapping to the same
- * slot in one call is undefined.  Supported: any dims whose RoPE part lies in
- * one 128-channel tile (true for d_latent = 512, d_rope = 64).
+ * slot in one call is undefined.
+ * workspace: device scratch of mla_cache_append_workspace_size() bytes
+ * (4-byte aligned; may be NULL when that size is 0).  bf16 activations take
+ * the matrix-core path (split-K partials in the workspace, then a per-token
+ * finalize); fp32 activations take a VALU path that needs no workspace and
+ * supports dims whose RoPE part lies in one 128-channel tile.
+ * Errors: MLA_ERR_WORKSPACE_TOO_SMALL if workspace_bytes is below the size.
  */
+size_t mla_cache_append_workspace_size(const mla_dims *dims, int32_t n_tokens, int32_t d_model);
+
 int mla_cache_append(const mla_dims *dims, const void *h, int32_t n_tokens, int32_t d_model,
                      const void *w_dkv, const void *w_kr, const int32_t *seq_ids,
                      const int32_t *positions, const int32_t *page_table,
                      int32_t max_blocks_per_seq, void *cache, float *cache_scales,
-                     mla_stream_t stream);
+                     void *workspace, size_t workspace_bytes, mla_stream_t stream);
 
 /*
  * Split-KV decode (mla_decode + mla_decode_combine).

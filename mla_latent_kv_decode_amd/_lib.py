@@ -24,7 +24,8 @@ ERR_UNSUPPORTED = -2
 ERR_WORKSPACE_TOO_SMALL = -3
 ERR_HIP = -4
 
-EXPORTS = ("mla_abi_version", "mla_last_error", "mla_device_cu_count", "mla_cache_append",
+EXPORTS = ("mla_abi_version", "mla_last_error", "mla_device_cu_count",
+           "mla_cache_append_workspace_size", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_combine", "mla_out_proj")
 
 
@@ -73,7 +74,10 @@ def lib():
         L.mla_abi_version.restype = ctypes.c_int
         L.mla_last_error.restype = ctypes.c_char_p
         L.mla_device_cu_count.restype = ctypes.c_int
-        L.mla_cache_append.argtypes = [D, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P]
+        L.mla_cache_append_workspace_size.argtypes = [D, _I, _I]
+        L.mla_cache_append_workspace_size.restype = ctypes.c_size_t
+        L.mla_cache_append.argtypes = [D, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P,
+                                       ctypes.c_size_t, _P]
         L.mla_decode_workspace_size.argtypes = [D, _I, _I, _I]
         L.mla_decode_workspace_size.restype = ctypes.c_size_t
         L.mla_decode.argtypes = [D, _P, _I, _I, _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P]
@@ -113,13 +117,19 @@ def mla_device_cu_count() -> int:
     return lib().mla_device_cu_count()
 
 
+def mla_cache_append_workspace_size(dims, n_tokens: int, d_model: int) -> int:
+    return lib().mla_cache_append_workspace_size(ctypes.byref(dims), n_tokens, d_model)
+
+
 def mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, page_table, cache,
-                     cache_scales=None, stream=None):
-    """h [T, d_model]; page_table [B, max_blocks]; cache [num_blocks, bs, D]."""
+                     cache_scales=None, workspace=None, stream=None):
+    """h [T, d_model]; page_table [B, max_blocks]; cache [num_blocks, bs, D];
+    workspace: a device tensor of mla_cache_append_workspace_size bytes (or None if 0)."""
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_cache_append(ctypes.byref(dims), _ptr(h), h.shape[0], h.shape[1], _ptr(w_dkv),
                                   _ptr(w_kr), _ptr(seq_ids), _ptr(positions), _ptr(page_table),
                                   page_table.shape[1], _ptr(cache), _ptr(cache_scales),
-                                  _stream(stream)))
+                                  _ptr(workspace), wsb, _stream(stream)))
 
 
 def mla_decode_workspace_size(dims, batch: int, n_q: int, num_partitions: int = 0) -> int:

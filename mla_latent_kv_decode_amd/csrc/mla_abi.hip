@@ -94,11 +94,38 @@ int mla_device_cu_count(void) {
   return n;
 }
 
+namespace {
+mla::AppendArgs append_args(const mla_dims* d, int32_t n_tokens, int32_t d_model) {
+  mla::AppendArgs a{};
+  a.n_tokens = n_tokens;
+  a.d_model = d_model;
+  a.d_latent = d->d_latent;
+  a.d_rope = d->d_rope;
+  a.D = d->d_latent + d->d_rope;
+  a.block_size = d->block_size;
+  a.cache_dtype = d->cache_dtype;
+  a.act_dtype = d->act_dtype;
+  a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  return a;
+}
+// The matrix-core append applies to bf16 activations (pointer alignment is
+// checked again at call time).
+bool append_uses_mfma(const mla::AppendArgs& a) {
+  return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024;
+}
+}  // namespace
+
+size_t mla_cache_append_workspace_size(const mla_dims* d, int32_t n_tokens, int32_t d_model) {
+  if (!d || n_tokens <= 0 || d_model < 1 || d->d_latent < 1 || d->d_rope < 0) return 0;
+  const mla::AppendArgs a = append_args(d, n_tokens, d_model);
+  return append_uses_mfma(a) ? mla::append_mfma_workspace(a) : 0;
+}
+
 int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t d_model,
                      const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
                      const int32_t* positions, const int32_t* page_table,
                      int32_t max_blocks_per_seq, void* cache, float* cache_scales,
-                     mla_stream_t stream) {
+                     void* workspace, size_t workspace_bytes, mla_stream_t stream) {
   if (int e = check_dims(d, true)) return e;
   if (n_tokens < 0 || d_model < 1 || max_blocks_per_seq < 1)
     return fail(MLA_ERR_INVALID_ARGUMENT, "n_tokens=%d d_model=%d max_blocks_per_seq=%d", n_tokens,
@@ -113,7 +140,7 @@ int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t
       !aligned(seq_ids, 4) || !aligned(positions, 4) || !aligned(page_table, 4) ||
       (cache_scales && !aligned(cache_scales, 4)))
     return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-  mla::AppendArgs a;
+  mla::AppendArgs a = append_args(d, n_tokens, d_model);
   a.h = h;
   a.w_dkv = w_dkv;
   a.w_kr = w_kr;
@@ -122,19 +149,22 @@ int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t
   a.page_table = page_table;
   a.cache = cache;
   a.scales = cache_scales;
-  a.n_tokens = n_tokens;
-  a.d_model = d_model;
-  a.d_latent = d->d_latent;
-  a.d_rope = d->d_rope;
-  a.D = d->d_latent + d->d_rope;
-  a.block_size = d->block_size;
   a.max_blocks = max_blocks_per_seq;
-  a.cache_dtype = d->cache_dtype;
-  a.act_dtype = d->act_dtype;
-  a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
-  if (!mla::append_supported(a))
-    return fail(MLA_ERR_UNSUPPORTED, "append: the RoPE part must lie in one 128-channel tile");
-  hipError_t e = mla::launch_append(a, static_cast<hipStream_t>(stream));
+  hipError_t e;
+  if (append_uses_mfma(a)) {
+    if (!mla::append_mfma_supported(a))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "append: bf16 h / weights must be 16-byte aligned");
+    const size_t need = mla::append_mfma_workspace(a);
+    if (workspace_bytes < need || (need && !workspace))
+      return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "append workspace %zu bytes < %zu required",
+                  workspace_bytes, need);
+    if (!aligned(workspace, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned workspace");
+    e = mla::launch_append_mfma(a, workspace, static_cast<hipStream_t>(stream));
+  } else {
+    if (!mla::append_supported(a))
+      return fail(MLA_ERR_UNSUPPORTED, "append: the RoPE part must lie in one 128-channel tile");
+    e = mla::launch_append(a, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return ok();
 }
@@ -250,7 +280,8 @@ int mla_out_proj(const mla_dims* d, const void* u, int32_t rows, const void* w_u
   a.d_latent = d->d_latent;
   a.d_v = d->d_v;
   a.act_dtype = d->act_dtype;
-  hipError_t e = mla::launch_out_proj(a, static_cast<hipStream_t>(stream));
+  hipError_t e = mla::out_proj_mfma_supported(a) ? mla::launch_out_proj_mfma(a, static_cast<hipStream_t>(stream))
+                                                 : mla::launch_out_proj_generic(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "out_proj launch");
   return ok();
 }

@@ -57,6 +57,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 bool append_supported(const AppendArgs& a);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
-hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t st);
+bool append_mfma_supported(const AppendArgs& a);
+size_t append_mfma_workspace(const AppendArgs& a);
+hipError_t launch_append_mfma(const AppendArgs& a, void* ws, hipStream_t st);
+hipError_t launch_out_proj_generic(const OutProjArgs& a, hipStream_t st);
+bool out_proj_mfma_supported(const OutProjArgs& a);
+hipError_t launch_out_proj_mfma(const OutProjArgs& a, hipStream_t st);
 
 }  // namespace mla

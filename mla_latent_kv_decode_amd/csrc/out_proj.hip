@@ -71,8 +71,4 @@ hipError_t launch_out_proj_generic(const OutProjArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t st) {
-  return launch_out_proj_generic(a, st);
-}
-
 }  // namespace mla

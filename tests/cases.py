@@ -22,6 +22,13 @@ def dims_of(cfg: W.Config, flags: int = 0, act: Optional[str] = None):
                        DT[cfg.cache_dtype], DT[act or cfg.act_dtype], flags=flags)
 
 
+def append_workspace(dims, n_tokens: int, d_model: int, device="cuda"):
+    """Device scratch for mla_cache_append (None when the path needs none)."""
+    import mla_latent_kv_decode_amd as M
+    n = M.mla_cache_append_workspace_size(dims, n_tokens, d_model)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def rel_l2(x, y) -> float:
     x = np.asarray(x, np.float64)
     y = np.asarray(y, np.float64)

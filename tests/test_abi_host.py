@@ -97,10 +97,14 @@ def test_other_entry_points_validate(L):
     assert lib.mla_out_proj(ctypes.byref(d), FAKE, -1, FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT
     assert lib.mla_out_proj(ctypes.byref(d), None, 4, FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT
     assert lib.mla_out_proj(ctypes.byref(d), FAKE, 0, FAKE, FAKE, None) == L.OK
-    assert lib.mla_cache_append(ctypes.byref(d), FAKE, 4, 7168, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
-                                FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT  # scales on bf16
-    straddle = _dims(L, d_latent=100)
-    assert lib.mla_cache_append(ctypes.byref(straddle), FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                16, FAKE, None, None) == L.ERR_UNSUPPORTED
-    assert lib.mla_cache_append(ctypes.byref(d), FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
-                                FAKE, None, None) == L.OK
+    ap = lambda dims, T=4, dm=7168, sc=None, ws=FAKE, wsb=1 << 30: lib.mla_cache_append(
+        dims, FAKE, T, dm, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, sc, ws, wsb, None)
+    assert ap(ctypes.byref(d), sc=FAKE) == L.ERR_INVALID_ARGUMENT           # scales on bf16
+    need = L.mla_cache_append_workspace_size(d, 4, 7168)
+    assert need > 0
+    assert ap(ctypes.byref(d), wsb=need - 1) == L.ERR_WORKSPACE_TOO_SMALL
+    assert ap(ctypes.byref(d), ws=None) == L.ERR_WORKSPACE_TOO_SMALL
+    f32 = _dims(L, d_latent=100, act_dtype=L.FP32, cache_dtype=L.FP32)       # VALU path
+    assert L.mla_cache_append_workspace_size(f32, 4, 64) == 0
+    assert ap(ctypes.byref(f32), dm=64, ws=None, wsb=0) == L.ERR_UNSUPPORTED  # RoPE straddles tiles
+    assert ap(ctypes.byref(d), T=0) == L.OK

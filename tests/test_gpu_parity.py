@@ -13,7 +13,8 @@ import torch
 
 import mla_workloads as W
 from oracle import mla_oracle as O
-from tests.cases import DT, DecodeCase, compare_sampled, dims_of, max_abs, rel_l2, to_f64
+from tests.cases import (DT, DecodeCase, append_workspace, compare_sampled, dims_of, max_abs,
+                         rel_l2, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,7 +116,8 @@ def test_append_identity_projection_bit_exact(cache_dtype):
         scales = None
     before = cache.clone()
     M.mla_cache_append(dims, h.cuda(), _t(w_dkv, tdt), _t(w_kr, tdt), _t(seq_ids, torch.int32),
-                       _t(positions, torch.int32), _t(table, torch.int32), cache, scales)
+                       _t(positions, torch.int32), _t(table, torch.int32), cache, scales,
+                       append_workspace(dims, T, D))
     torch.cuda.synchronize()
     pool = {"dtype": cache_dtype, "data": None}
     written = np.zeros((nblk, bs), bool)
@@ -170,12 +172,46 @@ def test_append_v3_random_weights_bf16():
     dims = dims_of(cfg)
     cache = torch.zeros((nblk, 64, d.row), dtype=torch.bfloat16, device="cuda")
     M.mla_cache_append(dims, h.cuda(), w_dkv.cuda(), w_kr.cuda(), _t(seq_ids, torch.int32),
-                       _t(positions, torch.int32), _t(table, torch.int32), cache)
+                       _t(positions, torch.int32), _t(table, torch.int32), cache,
+                       workspace=append_workspace(dims, T, d.d_model))
     torch.cuda.synchronize()
     want = O.kv_rows(to_f64(h), to_f64(w_dkv), to_f64(w_kr), positions)
     got = np.stack([to_f64(cache[table[b, 63], 63]) for b in range(T)])
     assert rel_l2(got, want) <= 4e-3
     assert max_abs(got, want) <= 2e-2
+
+
+@pytest.mark.parametrize("T", [1, 33, 512])
+def test_append_v3_fp8_random_weights(T):
+    """fp8 cache: the device quantises its own fp32 rows; compare the decoded
+    values with the oracle's rows (fp8 bar) and check every code's tile
+    scale is amax/448 of what was stored."""
+    import mla_latent_kv_decode_amd as M
+    d = W.V3
+    h = W.normal((T, d.d_model), 14).to(torch.bfloat16)
+    w_dkv = W.weight(d.d_latent, d.d_model, 15, dtype=torch.bfloat16)
+    w_kr = W.weight(d.d_rope, d.d_model, 16, dtype=torch.bfloat16)
+    lens = np.full(T, 300, np.int32)
+    table, nblk = W.page_table(lens, 64, seed=6, guard_blocks=1)
+    positions = np.random.default_rng(T).integers(0, 300, T).astype(np.int32)
+    seq_ids = np.arange(T, dtype=np.int32)
+    dims = dims_of(W.CONFIGS["fp8"])
+    cache = torch.zeros((nblk, 64, d.row), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((nblk, 64, 5), device="cuda")
+    M.mla_cache_append(dims, h.cuda(), w_dkv.cuda(), w_kr.cuda(), _t(seq_ids, torch.int32),
+                       _t(positions, torch.int32), _t(table, torch.int32), cache, scales,
+                       append_workspace(dims, T, d.d_model))
+    torch.cuda.synchronize()
+    want = O.kv_rows(to_f64(h), to_f64(w_dkv), to_f64(w_kr), positions)
+    got = []
+    for i in range(T):
+        blk, off = O.slot_of(table, i, int(positions[i]), 64)
+        c, sc = cache[blk, off].cpu().numpy(), scales[blk, off].cpu().numpy()
+        dec = O.dequantize_fp8_rows(c[None], sc[None])[0]
+        for k, (lo, hi) in enumerate(O.fp8_tiles(d.row)):
+            assert np.max(np.abs(c[lo:hi] & 0x7F)) == 0x7E  # the tile max encodes to 448
+        got.append(dec)
+    assert rel_l2(np.stack(got), want) <= 5e-2
 
 
 # --------------------------------------------------------------------------
