@@ -163,7 +163,8 @@ void decode_mfma_kernel(DecodeArgs a) {
     const int ntiles = max(0, u_end - ulo);
     const size_t orow0 = (size_t(slot) * a.n_q + j) * kH + wave * 32;
     if (ntiles == 0) {  // nothing visible to this query in the piece
-      for (int e = lane; e < 32 * kDC; e += kWave) a.ws_o[orow0 * kDC + e] = 0.f;
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.ws_o) + orow0 * kDC);
+      for (int e = lane; e < 32 * kDC / 8; e += kWave) dst[e] = uint4{0u, 0u, 0u, 0u};
       if (lane < 32) a.ws_lse[orow0 + lane] = -INFINITY;
       return;
     }
@@ -172,6 +173,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     auto block_ptr = [&](int u) {
       return cache + int64_t(__builtin_amdgcn_readfirstlane(pt[u])) * kTileBytes;
     };
+    auto block_at = [&](int blk) { return cache + int64_t(blk) * kTileBytes; };
     auto valid_in = [&](int u) { return min(kBS, nvis - u * kBS); };
 
     const int loff[2] = {load_lane_off(lane, 0), load_lane_off(lane, 1)};
@@ -207,13 +209,18 @@ void decode_mfma_kernel(DecodeArgs a) {
       l_run = 0.f;
       bool redo = false;
       if (threadIdx.x == 0) sm.redo = 0;
+      // page-table entry of the tile after next, fetched one iteration early
+      // so the lookup never sits on the critical path of a prefetch
+      int blk_next = ntiles > 1 ? pt[ulo + 1] : 0;
       for (int it = 0; it < ntiles; ++it) {
         const int u = ulo + it;
         wait_vm();
         __syncthreads();  // tile `it` landed for every wave; buffer (it+1)%2 is free
         if (sm.redo) { redo = true; break; }
         if (it + 1 < ntiles)
-          load_tile(sm.tile[(it + 1) & 1], block_ptr(u + 1), valid_in(u + 1), wave, loff);
+          load_tile(sm.tile[(it + 1) & 1], block_at(__builtin_amdgcn_readfirstlane(blk_next)),
+                    valid_in(u + 1), wave, loff);
+        if (it + 2 < ntiles) blk_next = pt[u + 2];
         const unsigned char* tb = sm.tile[it & 1];
         const int nv = valid_in(u);
 
@@ -290,7 +297,9 @@ void decode_mfma_kernel(DecodeArgs a) {
         for (int n = 0; n < 4; ++n) vr[n] = vfrag(n);
 #pragma unroll
         for (int n = 0; n < kPV; ++n) {
-          O[n & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[n >> 4], vr[n & 3], O[n & 15], 0, 0, 0);
+          // O^T[channel][head] += V^T . P^T: the lane keeps one head, so the
+          // normalisation and the partial store need no cross-lane traffic
+          O[n & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[n & 3], pf[n >> 4], O[n & 15], 0, 0, 0);
           if (n + 4 < kPV) vr[n & 3] = vfrag(n + 4);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -306,18 +315,22 @@ void decode_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();  // buffers are reused by the next piece
 
-    // ---- epilogue: normalise and write the partial ----
+    // ---- epilogue: normalise and write the partial (bf16) ----
+    // lane (g, hl) holds O^T rows = channels 32*cb + 8*rg + 4*g + {0..3} of head hl
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
     if (lane < 32) a.ws_lse[orow0 + lane] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+    uint16_t* orow = static_cast<uint16_t*>(a.ws_o) + (orow0 + hl) * kDC + 4 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hr = 8 * (r / 4) + 4 * g + (r % 4);
-      const float ir = __shfl(inv, hr, 64);
-      float* orow = a.ws_o + (orow0 + hr) * kDC + hl;
+    for (int cb = 0; cb < kDC / 32; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < kDC / 32; ++cb) orow[32 * cb] = O[cb][r] * ir;
-    }
+      for (int rg = 0; rg < 4; ++rg) {
+        const uint32_t lo = uint32_t(f32_to_bf16(O[cb][4 * rg + 0] * inv)) |
+                            (uint32_t(f32_to_bf16(O[cb][4 * rg + 1] * inv)) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16(O[cb][4 * rg + 2] * inv)) |
+                            (uint32_t(f32_to_bf16(O[cb][4 * rg + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * cb + 8 * rg) = uint2{lo, hi};
+      }
   });
 }
 

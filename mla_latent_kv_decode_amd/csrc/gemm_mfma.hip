@@ -104,13 +104,37 @@ __global__ __launch_bounds__(kNT) void append_partial_kernel(AppendArgs a, float
 template <int CDT>
 __global__ __launch_bounds__(kNT) void append_finalize_kernel(AppendArgs a, const float* ws, int nk) {
   __shared__ float y[1024];
-  __shared__ float red[8];
+  __shared__ float4 part[4][256];
   const int t = blockIdx.x, tid = threadIdx.x;
-  const int D = a.D, dc = a.d_latent;
-  for (int c = tid; c < D; c += kNT) {
-    float s = 0.f;
-    for (int kc = 0; kc < nk; ++kc) s += ws[(int64_t(kc) * a.n_tokens + t) * D + c];
-    y[c] = s;
+  const int D = a.D, dc = a.d_latent, D4 = D / 4;
+  // sum of the k-slice partials: 4 groups of 64 threads split the slices,
+  // each thread owns float4 column quads q, q+64, ...; loads are independent
+  {
+    const int q = tid % 64, grp = tid / 64;
+    const float4* w4 = reinterpret_cast<const float4*>(ws);
+    for (int cq = q; cq < D4; cq += 64) {
+      float4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      int kc = grp;
+      for (; kc + 4 < nk; kc += 8) {
+        const float4 x0 = w4[(int64_t(kc) * a.n_tokens + t) * D4 + cq];
+        const float4 x1 = w4[(int64_t(kc + 4) * a.n_tokens + t) * D4 + cq];
+        s0.x += x0.x; s0.y += x0.y; s0.z += x0.z; s0.w += x0.w;
+        s1.x += x1.x; s1.y += x1.y; s1.z += x1.z; s1.w += x1.w;
+      }
+      if (kc < nk) {
+        const float4 x0 = w4[(int64_t(kc) * a.n_tokens + t) * D4 + cq];
+        s0.x += x0.x; s0.y += x0.y; s0.z += x0.z; s0.w += x0.w;
+      }
+      part[grp][cq] = float4{s0.x + s1.x, s0.y + s1.y, s0.z + s1.z, s0.w + s1.w};
+    }
+  }
+  __syncthreads();
+  for (int cq = tid; cq < D4; cq += kNT) {
+    const float4 a0 = part[0][cq], a1 = part[1][cq], a2 = part[2][cq], a3 = part[3][cq];
+    y[4 * cq + 0] = (a0.x + a1.x) + (a2.x + a3.x);
+    y[4 * cq + 1] = (a0.y + a1.y) + (a2.y + a3.y);
+    y[4 * cq + 2] = (a0.z + a1.z) + (a2.z + a3.z);
+    y[4 * cq + 3] = (a0.w + a1.w) + (a2.w + a3.w);
   }
   __syncthreads();
   const int pos = a.positions[t];
@@ -146,7 +170,6 @@ __global__ __launch_bounds__(kNT) void append_finalize_kernel(AppendArgs a, cons
       if (lane == 0) a.scales[row * ntiles + k] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
     }
   }
-  (void)red;
 }
 
 }  // namespace
@@ -175,7 +198,7 @@ static void append_split(const AppendArgs& a, int* nk, int* kchunk) {
 }
 
 bool append_mfma_supported(const AppendArgs& a) {
-  return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024 &&
+  return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024 && a.D % 4 == 0 &&
          (reinterpret_cast<uintptr_t>(a.h) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.w_dkv) % 16) == 0 &&
          (a.d_rope == 0 || (reinterpret_cast<uintptr_t>(a.w_kr) % 16) == 0);
 }

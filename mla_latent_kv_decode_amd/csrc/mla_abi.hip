@@ -72,7 +72,7 @@ struct WsLayout {
 WsLayout ws_layout(const mla_dims* d, int batch, int n_q, int G) {
   const size_t slots = mla::ws_slots(batch, G);
   WsLayout w;
-  w.o_bytes = slots * size_t(n_q) * d->num_heads * d->d_latent * sizeof(float);
+  w.o_bytes = slots * size_t(n_q) * d->num_heads * d->d_latent * elem_bytes(d->act_dtype);
   w.lse_off = align_up(w.o_bytes, 256);
   w.total = align_up(w.lse_off + slots * size_t(n_q) * d->num_heads * sizeof(float), 256);
   return w;
@@ -111,7 +111,7 @@ mla::AppendArgs append_args(const mla_dims* d, int32_t n_tokens, int32_t d_model
 // The matrix-core append applies to bf16 activations (pointer alignment is
 // checked again at call time).
 bool append_uses_mfma(const mla::AppendArgs& a) {
-  return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024;
+  return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024 && a.D % 4 == 0;
 }
 }  // namespace
 
@@ -204,7 +204,7 @@ int mla_decode(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, con
   a.scales = cache_scales;
   a.page_table = page_table;
   a.seq_lens = seq_lens;
-  a.ws_o = static_cast<float*>(workspace);
+  a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.lse_off);
   a.batch = batch;
   a.n_q = n_q;
@@ -245,7 +245,7 @@ int mla_decode_combine(const mla_dims* d, const void* workspace, size_t workspac
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes,
                 w.total);
   mla::CombineArgs a;
-  a.ws_o = static_cast<const float*>(workspace);
+  a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.lse_off);
   a.seq_lens = seq_lens;
   a.u = u_out;

@@ -236,7 +236,8 @@ MLA_DEV void plan_lookup(const int32_t* seq_lens, int B, int bs, int G, int b,
   }
 }
 
-// Workspace layout: [o: n_slots][n_q][H][d_latent] fp32 | [lse: n_slots][n_q][H] fp32.
+// Workspace layout: [o: n_slots][n_q][H][d_latent] in the activation dtype |
+// [lse: n_slots][n_q][H] fp32.
 struct Workspace {
   float* o;
   float* lse;

@@ -11,7 +11,7 @@ struct DecodeArgs {
   const float* scales;     // [nblk][bs][ntiles] (fp8) or null
   const int32_t* page_table;
   const int32_t* seq_lens;
-  float* ws_o;             // [slots][n_q][H][d_latent]
+  void* ws_o;              // [slots][n_q][H][d_latent] act dtype (normalised partials)
   float* ws_lse;           // [slots][n_q][H]
   int batch, n_q, H, D, d_latent, block_size, max_blocks, G;
   int cache_dtype, act_dtype;
@@ -19,7 +19,7 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-  const float* ws_o;
+  const void* ws_o;        // act dtype
   const float* ws_lse;
   const int32_t* seq_lens;
   void* u;                 // [B][n_q][H][d_latent] act dtype

@@ -80,7 +80,7 @@ def test_workspace_size_closed_form(L):
     d = _dims(L)
     B, n_q, G, H, dc = 64, 1, 256, 128, 512
     slots = B + G
-    o = slots * n_q * H * dc * 4
+    o = slots * n_q * H * dc * 2          # partials are stored in the bf16 activation dtype
     lse = slots * n_q * H * 4
     want = (((o + 255) // 256 * 256 + lse) + 255) // 256 * 256
     assert L.mla_decode_workspace_size(d, B, n_q, G) == want
