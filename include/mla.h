@@ -4,8 +4,9 @@
  * Multi-head latent attention (MLA) decode in the matrix-absorbed form over a
  * paged latent cache, as described on the page "DeepSeek MLA Architecture:
  * How Multi-Head Latent Attention Cuts KV Cache by 93%" (below: [MLA-93]),
- * sections "Core Mechanics" 1-3, "Total Cached Scalars per Token" and the
- * single-token decoding listing, and on "DeepSeek-V3 Architecture: Multi-Head
+ * sections "DeepSeek MLA Deep Dive: Core Mechanics" 1-3, "Total Cached
+ * Scalars per Token" and "Production PyTorch Implementation: Single-Token MLA
+ * Decoding" (below: [MLA-93] decoding section), and on "DeepSeek-V3 Architecture: Multi-Head
  * Latent Attention (MLA) & FP8 Mixed-Precision Training" (below: [V3-ARCH]),
  * sections 2, A and 3.
  *
@@ -97,7 +98,8 @@ int mla_device_cu_count(void);
 /*
  * mla_cache_append -- project, rotate and store new tokens' cache rows.
  * [MLA-93] Core Mechanics 1 (c = W^DKV h) and 3 (k^R = RoPE(W^KR h), shared
- * by all heads); decoding listing STEP 1.  RoPE is rotate-half: channel j of
+ * by all heads); in the [MLA-93] decoding section the new token's latent and
+ * RoPE key are cached before attention.  RoPE is rotate-half: channel j of
  * k^R is paired with j + d_rope/2 and rotated by pos * base^(-j/(d_rope/2)).
  *
  *   h          [n_tokens][d_model]        act_dtype
@@ -135,9 +137,10 @@ int mla_cache_append(const mla_dims *dims, const void *h, int32_t n_tokens, int3
  * query position ([MLA-93] Core Mechanics 3).  Query j of sequence b sits at
  * position seq_lens[b] - n_q + j and attends to positions
  * 0 .. seq_lens[b] - n_q + j (itself included: the new tokens are appended
- * before attention, decoding listing STEP 1 then STEP 4).  Per head i:
+ * before attention, as in the [MLA-93] decoding section).  Per head i:
  *   s_t = scale * (q~_i . c_t + q^R_i . k^R_t),  p = softmax_t(s),
- *   u_i = sum_t p_t c_t  in R^{d_latent}        (listing STEPs 4-5).
+ *   u_i = sum_t p_t c_t  in R^{d_latent}   (attention and value aggregation in
+ *                                          latent space, [MLA-93] decoding section).
  *
  * The cache blocks of all sequences are laid end to end and cut into
  * `num_partitions` near-equal ranges; one workgroup per (range, query token)
@@ -145,9 +148,12 @@ int mla_cache_append(const mla_dims *dims, const void *h, int32_t n_tokens, int3
  * (o = normalised latent output, lse = natural-log sum of exp of the scores)
  * into `workspace`.  mla_decode_combine merges the pieces of each sequence
  * with a log-sum-exp weighting.  num_partitions <= 0 selects the default
- * (the device's compute-unit count divided by n_q, at least 1).  Results are
- * deterministic for a fixed num_partitions.
+ * (the device's compute-unit count divided by n_q, at least 1); values above
+ * MLA_MAX_PARTITIONS are rejected with MLA_ERR_INVALID_ARGUMENT (and give a
+ * workspace size of 0).  Results are deterministic for a fixed num_partitions.
  */
+#define MLA_MAX_PARTITIONS (1 << 20)
+
 size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch, int32_t n_q,
                                  int32_t num_partitions);
 
@@ -168,7 +174,7 @@ int mla_decode_combine(const mla_dims *dims, const void *workspace, size_t works
 
 /*
  * mla_out_proj -- per-head value up-projection o_i = W^UV_i u_i.
- * [MLA-93] decoding listing STEP 5 (W^UV applied to the latent output).
+ * [MLA-93] decoding section (W^UV applied to the latent output).
  *   u     [rows][num_heads][d_latent] act_dtype  (rows = batch * n_q)
  *   w_uv  [num_heads][d_v][d_latent]  act_dtype
  *   out   [rows][num_heads][d_v]      act_dtype

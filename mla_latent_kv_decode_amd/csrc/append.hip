@@ -1,6 +1,6 @@
 // Cache append: c = W^DKV h, k^R = RoPE(W^KR h, pos), row [c ; k^R] written to
-// the token's paged slot ([MLA-93] Core Mechanics 1 and 3; decoding listing
-// STEP 1), optionally quantised to e4m3 with one fp32 scale per 128-channel
+// the token's paged slot ([MLA-93] Core Mechanics 1 and 3; decoding
+// section), optionally quantised to e4m3 with one fp32 scale per 128-channel
 // tile of the row.
 //
 // One workgroup per (16-token tile, 128-column tile).  Column tiles coincide

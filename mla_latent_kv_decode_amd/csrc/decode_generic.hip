@@ -3,7 +3,7 @@
 // One workgroup per (partition g, query token j, head i).  For every piece of
 // its partition it runs an online softmax over 64-token tiles:
 //   s_t = scale * (q~ . c_t + q^R . k^R_t)       ([MLA-93] Core Mechanics 3)
-//   u   = sum_t softmax(s)_t c_t                 (decoding listing STEPs 4-5)
+//   u   = sum_t softmax(s)_t c_t                 ([MLA-93] decoding section)
 // and writes the piece's normalised output and log-sum-exp to the workspace.
 // This path serves small or unusual dims (and fp32), and is an independent
 // second GPU implementation for cross-checking the MFMA kernel.
@@ -52,8 +52,7 @@ __global__ __launch_bounds__(kGenNT) void decode_generic_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
 
   plan_for_each_piece<kGenNT>(a.seq_lens, a.batch, bs, a.G, g, plan,
-                              [&](int b, int ulo, int uhi, int slot) {
-    const int L = a.seq_lens[b];
+                              [&](int b, int ulo, int uhi, int slot, int L) {
     const int nvis = L - a.n_q + j + 1;  // positions 0 .. L - n_q + j
     const int t_begin = ulo * bs;
     const int t_end = min(uhi * bs, nvis);

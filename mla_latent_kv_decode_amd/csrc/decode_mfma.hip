@@ -2,39 +2,49 @@
 // H = 128 heads, d_c = 512, d_R = 64 (row D = 576), 64-token cache blocks,
 // bf16 queries and cache, fp32 accumulation.
 //
-// What it computes ([MLA-93] Core Mechanics 3, decoding listing STEPs 4-5):
-// for every head i, s_t = scale * ([q~_i ; q^R_i] . [c_t ; k^R_t]),
-// p = softmax(s), u_i = sum_t p_t c_t -- here per piece of a partition of the
-// cache blocks, written as (normalised u, log-sum-exp) partials.
+// What it computes ("DeepSeek MLA Architecture: How Multi-Head Latent
+// Attention Cuts KV Cache by 93%", Core Mechanics 3 and its single-token
+// decoding section): for every head i,
+// s_t = scale * ([q~_i ; q^R_i] . [c_t ; k^R_t]), p = softmax(s),
+// u_i = sum_t p_t c_t -- here per piece of a partition of the cache blocks,
+// written as (normalised u, log-sum-exp) partials.
 //
 // Design (one workgroup of 4 waves per (partition, query token)):
-//  * All 128 heads share one 64-token tile of the cache.  The tile
-//    (64 x 576 bf16 = 72 KB) moves HBM -> LDS once with direct-to-LDS 16-byte
-//    loads (global_load_lds_dwordx4), double-buffered, and every wave reads it
-//    for its own 32 heads, so each cache byte crosses HBM once per step.
+//  * All 128 heads share the cache.  The kernel walks the piece in steps of
+//    32 tokens (half a cache block, 36 KB); each step moves HBM -> LDS once
+//    with direct-to-LDS 16-byte buffer loads and every wave reads it for its
+//    own 32 heads, so each cache byte crosses HBM once.
+//  * Software pipeline over four LDS step buffers: iteration h computes the
+//    scores of step h, then the output update of step h-1 with the softmax of
+//    step h interleaved between those MFMAs (the VALU work runs under matrix
+//    work), while steps h+1 and h+2 are in flight.
 //  * Scores as S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: the K fragment (32
 //    tokens x 16 channels) comes from LDS as one ds_read_b128 per lane, Q^T
 //    (16 channels x 32 heads) stays in registers for the whole piece.  In the
-//    S^T accumulator a lane owns one head and 32 of the 64 tokens, so the
+//    S^T accumulator a lane owns one head and 16 of the 32 tokens, so the
 //    softmax row max is an in-lane reduction plus one exchange with lane^32,
-//    and the accumulator already has the A-operand layout of the P.V product
-//    (the token order inside each K=16 step is a permutation we mirror on V).
-//  * P.V: O[32 heads x 512] += P[32 x 16 tokens] . V[16 tokens x 32 channels]
-//    with V read from the same token-major tile by ds_read_b64_tr_b16 (each
-//    16-lane group turns a 4-token x 16-channel block into per-lane columns).
+//    and the accumulator already has the layout of the P operand of P.V (the
+//    token order inside each K=16 step is a permutation mirrored on V).
+//  * O^T[channel][head] += V^T . P^T with the V^T fragment read from the same
+//    token-major step by ds_read_b64_tr_b16 (each 16-lane group turns a
+//    4-token x 16-channel block into per-lane columns).  O^T lives in the
+//    AGPRs (256 per lane) and keeps one head per lane, so the epilogue needs
+//    no cross-lane traffic.
 //  * Softmax in log2 units against a per-head reference m_ref taken from the
-//    head's first tile: p = 2^(s' - m_ref).  While every later score stays
-//    below m_ref + kHeadroom (32), p <= 2^32 and nothing can overflow in fp32
-//    or bf16, so O never needs rescaling and is only ever touched by MFMA.  If
-//    some head exceeds its headroom, the workgroup raises that head's
-//    reference and recomputes the piece (correct for any input; it does not
+//    head's first step: p = 2^(s' - m_ref).  While later scores stay below
+//    m_ref + kHeadroom (32), p <= 2^32 and nothing can overflow in fp32 or
+//    bf16, so O is only ever touched by MFMA.  A head that exceeds it moves
+//    its reference to the new maximum and its wave rescales O and the running
+//    sum by 2^(old - new) (the exact online-softmax update; it does not
 //    happen for ordinary logits).
-//  * Masked (past-length) tokens: their score is -inf, and their tile rows are
+//  * Masked (past-length) tokens: their score is -inf, and their rows lie
 //    outside the load's buffer range, which fills them with zeros, so
 //    0 * (stale value / NaN) never reaches the accumulators.
-//  * LDS tile layout: 8-token x 8-chunk sub-blocks (one 1 KB direct load
+//  * LDS step layout: 8-token x 8-chunk sub-blocks (one 1 KB direct load
 //    each), 16-byte chunks XOR-swizzled by token so both the b128 K reads and
 //    the transposed V reads spread over all banks.
+//  * The partial is transposed through LDS in the epilogue and written with
+//    whole-row non-temporal stores.
 #include <utility>
 
 #include "mla_internal.h"
@@ -43,76 +53,112 @@ namespace mla {
 namespace {
 
 constexpr int kH = 128, kDC = 512, kDR = 64, kD = kDC + kDR, kBS = 64;
-constexpr int kNT = 256;                  // 4 waves x 32 heads
-constexpr int kChunks = kD / 8;           // 72 chunks of 16 B per token row
-constexpr int kRowBytes = kD * 2;         // 1152
-constexpr int kTileBytes = kBS * kRowBytes;  // 73728
-constexpr int kLoadsPerWave = (kTileBytes / 1024) / 4;  // 18 direct loads of 1 KB
-constexpr float kHeadroom = 32.0f;        // log2 headroom above the reference max
+constexpr int kNT = 256;                      // 4 waves x 32 heads
+constexpr int kStep = 32;                     // tokens per step
+constexpr int kRowBytes = kD * 2;             // 1152
+constexpr int kBlockBytes = kBS * kRowBytes;  // 73728
+constexpr int kStepBytes = kStep * kRowBytes; // 36864 = 36 sub-blocks of 1 KB
+constexpr int kNBuf = 4;                      // LDS step buffers: h-1 (PV), h (QK), h+1, h+2 in flight
+constexpr int kLoadsPerWave = 9;              // 1 KB direct loads per wave per step
+constexpr float kHeadroom = 32.0f;            // log2 headroom above the reference max
+constexpr int kStageRow = kDC * 2 + 16;       // epilogue transpose row (padded against bank conflicts)
+constexpr int kQK = kD / 16;                  // score MFMAs per step
+constexpr int kPV = 2 * (kDC / 32);           // output MFMAs per step
+constexpr int kRK = 4, kRV = 4;               // LDS operand fragments read ahead of their MFMA
+static_assert(4 * 32 * kStageRow <= kNBuf * kStepBytes, "epilogue stage must fit the step buffers");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 // 16-byte-chunk swizzle: chunk slot (c & 7) ^ swz(t) within token t's sub-row.
 MLA_DEV int swz(int t) { return ((((t & 3) << 1) | ((t >> 2) & 1)) ^ ((t >> 2) & 2)) & 7; }
 
-// Byte offset of chunk c (0..71) of token t (0..63) inside a tile buffer.
-MLA_DEV int tile_off(int t, int c) {
+// Byte offset of chunk c (0..71) of token t (0..31) inside a step buffer.
+MLA_DEV int step_off(int t, int c) {
   return (((t >> 3) * 9 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz(t))) * 16;
 }
 
 struct Smem {
-  alignas(16) unsigned char tile[2][kTileBytes];
+  alignas(128) unsigned char buf[kNBuf][kStepBytes];  // kStepBytes is a multiple of 128
   PlanScratch<kNT> plan;
-  int redo;  // a head exceeded its headroom: recompute the piece
 };
 
-MLA_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+MLA_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// Per-lane byte offset, inside an 8-token group, of the chunk this lane loads
-// in sub-block column cg: token row lane/8, swizzled chunk slot lane%8.  The
-// group parity p = (token group & 1) selects the swizzle variant.
+// Workgroup barrier for the step loop.  __syncthreads() carries a workgroup
+// fence, which makes the compiler wait for *all* outstanding vector-memory
+// operations -- including the prefetches of later steps.  The step loop needs
+// less: its own LDS traffic complete (lgkmcnt) and the explicit vmcnt wait for
+// the current step that precedes each call.  The memory clobber keeps memory
+// accesses from moving across it.
+MLA_DEV void step_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Per-lane byte offset (inside its 8-token group) of the chunk it loads;
+// the group parity p selects the swizzle variant.
 MLA_DEV int load_lane_off(int lane, int p) {
   const int t = 8 * p + lane / 8;
   return (lane / 8) * kRowBytes + ((lane & 7) ^ swz(t)) * 16;
 }
 
-// Issue this wave's 18 direct HBM->LDS loads (1 KB sub-blocks) of one cache
-// block.  The buffer descriptor covers only the `nvalid` live rows: lanes whose
-// row is past it read out of range, which writes zeros into LDS, so masked
-// rows never carry stale or NaN data into the products.
+// This wave's 9 direct HBM->LDS loads of one step: token group `wave`
+// (8 tokens) x 9 column groups.  The descriptor covers only the live rows, so
+// lanes past `nvalid` read out of range, which writes zeros into LDS.
+// The loads are issued from inline asm on purpose: the compiler cannot tell
+// that the LDS reads of the current step never touch the buffers these loads
+// fill, and would otherwise wait for *every* pending load (vmcnt(0)) before
+// each of them.  The step loop waits for exactly the loads it needs (wait_vm).
+// No register is written by these instructions (the data goes to LDS).  The
+// column offset goes into soffset: an immediate offset would also shift the
+// LDS destination.
 template <int M>
-MLA_DEV void load_one(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, const int (&loff)[2]) {
-  constexpr int cg = M % 9, par = M / 9;  // k = 18*wave + M -> tg = 2*wave + M/9
-  const int k = wave * kLoadsPerWave + M;
-  // the column-group offset goes into soffset: the instruction's immediate
-  // offset would also shift the LDS destination
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + k * 1024),
-                                           16, loff[par], (2 * wave + par) * 9216 + cg * 128, 0, 0);
+MLA_DEV void load_one(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, int loff) {
+  const int k = wave * kLoadsPerWave + M;  // sub-block (token group `wave`, column group M)
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) unsigned char*)(dst + k * 1024)));
+  // s_nop: one wait state between the M0 write and its use by the LDS DMA
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(loff), "s"(r), "s"(wave * 9216 + M * 128), "{m0}"(lds)
+               : "memory");
 }
 template <int... Ms>
-MLA_DEV void load_all(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, const int (&loff)[2],
+MLA_DEV void load_all(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, int loff,
                       std::integer_sequence<int, Ms...>) {
   (load_one<Ms>(r, dst, wave, loff), ...);
 }
-MLA_DEV void load_tile(unsigned char* dst, const unsigned char* src, int nvalid, int wave,
-                       const int (&loff)[2]) {
+MLA_DEV void load_step(unsigned char* dst, const unsigned char* src, int nvalid, int wave, int loff) {
   __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nvalid * kRowBytes, 0x00020000);
   load_all(r, dst, wave, loff, std::make_integer_sequence<int, kLoadsPerWave>{});
 }
 
-MLA_DEV bf16x8 lds_b128(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+MLA_DEV uint32_t lds_addr(const unsigned char* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const lds_u8*)p));
+}
+MLA_DEV bf16x8 lds_b128_at(uint32_t addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
+
+MLA_DEV bf16x8 lds_tr_pair_at(uint32_t p0, uint32_t p1) {
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 // Score MFMAs are written as inline asm with the accumulator constrained to
 // arch VGPRs: O needs the whole AGPR file, and the compiler would otherwise
-// place the scores in AGPRs and shuttle O blocks through VGPRs every tile.
+// place the scores in AGPRs and shuttle O blocks through VGPRs every step.
 // Hazards the compiler cannot see are handled explicitly: the chain starts
-// from a literal-zero accumulator (no VALU->MFMA dependency), successive
-// accumulations into one block are always separated by an independent MFMA,
-// and scores_ready() puts 24 wait states (more than the longest
+// from a literal-zero accumulator (no VALU->MFMA dependency), and
+// scores_ready() puts 24 wait states (more than the longest
 // MFMA-write -> VALU-read requirement) between the last write and the softmax.
 MLA_DEV void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
@@ -120,27 +166,31 @@ MLA_DEV void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
 MLA_DEV void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-MLA_DEV void scores_ready(f32x16& s0, f32x16& s1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+MLA_DEV void scores_ready(f32x16& s) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s)); }
+// Output MFMAs with the accumulator pinned to AGPRs: left to itself the
+// register allocator keeps some O blocks in VGPRs and copies them into AGPRs
+// around every MFMA, which pushes Q out of registers.  Consecutive updates of
+// one accumulator are exactly overlapping (hardware forwards them); the only
+// other readers and writers of O (zeroing, epilogue) sit behind o_ready().
+MLA_DEV void mfma_pv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-
-MLA_DEV bf16x8 lds_tr_pair(const unsigned char* p0, const unsigned char* p1) {
-  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, v);
+MLA_DEV void o_ready(f32x16 (&O)[16]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]),
+                 "+a"(O[6]), "+a"(O[7]), "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]),
+                 "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
 }
 
 __global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int g = lane / 32;       // lane group: which 8-wide half of a 16-wide k step
-  const int hl = lane % 32;      // head within the wave (S^T column)
+  const int hl = lane % 32;      // head within the wave (S^T / O^T column)
 
   // XCD-aware mapping: consecutive logical ids share an XCD (workgroups are
   // dealt round-robin to the 8 XCDs), so the n_q workgroups of a partition and
@@ -152,185 +202,222 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   const float c_log2 = a.scale * 1.4426950408889634f;  // scores -> log2 units
 
+  // Per-lane LDS offsets inside a step buffer, one register each; the
+  // other fragments follow from the swizzle's structure:
+  //  K fragment a (token hl, chunk 2a + g):   koff0 ^ (a << 5)
+  //  V fragment (transposed read; token 8*sec + 4*g + s16/4, chunk
+  //  4*cbo + 2*h16 + (s16%4)/2, half s16%2):   (voff0 ^ (cbo << 6) ^ (sec << 5)) + sec * 9216
+  // (+8 tokens moves one 8-token group down and flips swizzle bit 1).  Step
+  // buffers are 128-byte aligned, so the XORs commute with adding the base.
+  const int h16 = (lane / 16) & 1, s16 = lane % 16;
+  const uint32_t koff0 = uint32_t(step_off(hl, g));
+  const uint32_t voff0 = uint32_t(step_off(4 * g + s16 / 4, 2 * h16 + (s16 % 4) / 2) + 8 * (s16 % 2));
+  const int loff = load_lane_off(lane, wave & 1);
+
   plan_for_each_piece<kNT>(a.seq_lens, a.batch, kBS, a.G, part, sm.plan,
-                           [&](int b_, int ulo_, int uhi_, int slot_) {
+                           [&](int b_, int ulo_, int uhi_, int slot_, int L_) {
     // piece bounds come from LDS: tell the compiler they are wave-uniform
     const int b = __builtin_amdgcn_readfirstlane(b_), ulo = __builtin_amdgcn_readfirstlane(ulo_);
     const int uhi = __builtin_amdgcn_readfirstlane(uhi_), slot = __builtin_amdgcn_readfirstlane(slot_);
-    const int L = a.seq_lens[b];
-    const int nvis = L - a.n_q + j + 1;
-    const int u_end = min(uhi, (nvis + kBS - 1) / kBS);
-    const int ntiles = max(0, u_end - ulo);
+    const int L = __builtin_amdgcn_readfirstlane(L_);
+    const int nvis = L - a.n_q + j + 1;               // visible positions 0 .. nvis-1
+    const int t_lo = ulo * kBS;
+    const int t_hi = min(uhi * kBS, nvis);
+    const int nsteps = max(0, (t_hi - t_lo + kStep - 1) / kStep);
     const size_t orow0 = (size_t(slot) * a.n_q + j) * kH + wave * 32;
-    if (ntiles == 0) {  // nothing visible to this query in the piece
+    if (nsteps == 0) {  // nothing visible to this query in the piece
       uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.ws_o) + orow0 * kDC);
       for (int e = lane; e < 32 * kDC / 8; e += kWave) dst[e] = uint4{0u, 0u, 0u, 0u};
       if (lane < 32) a.ws_lse[orow0 + lane] = -INFINITY;
       return;
     }
-    const int32_t* pt = a.page_table + int64_t(b) * a.max_blocks;
+    // page table through the constant address space: scalar loads
+    const_i32* pt = (const_i32*)(uintptr_t)(a.page_table + int64_t(b) * a.max_blocks);
     const unsigned char* cache = static_cast<const unsigned char*>(a.cache);
-    auto block_ptr = [&](int u) {
-      return cache + int64_t(__builtin_amdgcn_readfirstlane(pt[u])) * kTileBytes;
+    auto step_at = [&](int blk, int h) {  // first byte of step h, which lies in block blk
+      return cache + int64_t(blk) * kBlockBytes + (h & 1) * kStepBytes;
     };
-    auto block_at = [&](int blk) { return cache + int64_t(blk) * kTileBytes; };
-    auto valid_in = [&](int u) { return min(kBS, nvis - u * kBS); };
+    auto valid_in = [&](int h) { return min(kStep, t_hi - (t_lo + h * kStep)); };
+    const int blk0 = pt[ulo];  // steps 0 and 1 lie in the piece's first block
 
-    const int loff[2] = {load_lane_off(lane, 0), load_lane_off(lane, 1)};
-    // first tile in flight while Q is fetched
-    load_tile(sm.tile[0], block_ptr(ulo), valid_in(ulo), wave, loff);
+    // Q^T fragments for this wave's 32 heads, resident for the whole piece
     const __bf16* qrow = static_cast<const __bf16*>(a.q) +
                          ((size_t(b) * a.n_q + j) * kH + wave * 32 + hl) * kD;
-    bf16x8 qf[kD / 16];
+    bf16x8 qf[kQK];
 #pragma unroll
-    for (int s = 0; s < kD / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * g);
-
-    // per-lane LDS offsets (tile-independent parts)
-    //  K fragment: token t = 32*bt + hl, chunk c = 2*s + g
-    int koff[4];
+    for (int s = 0; s < kQK; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * g);
+    // step 0 travels with Q; waiting for Q here (the compiler waits for every
+    // older load) keeps that wait from draining later steps inside the loop
+    load_step(sm.buf[0], step_at(blk0, 0), valid_in(0), wave, loff);
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) koff[a4] = tile_off(hl, 2 * a4 + g);
-    //  V fragment (transposed read): token 16*i + 8*sec + 4*g + s16/4,
-    //  channel 32*cb + 16*h + 4*(s16%4)
-    const int h16 = (lane / 16) & 1, s16 = lane % 16;
-    int voff[2][2];
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec)
-#pragma unroll
-      for (int cbo = 0; cbo < 2; ++cbo)
-        voff[sec][cbo] = tile_off(8 * sec + 4 * g + s16 / 4, 4 * cbo + 2 * h16 + (s16 % 4) / 2) +
-                         8 * (s16 % 2);
+    for (int s = 0; s < kQK; ++s) asm volatile("" ::"v"(qf[s]));
 
     f32x16 O[kDC / 32];
+#pragma unroll
+    for (int cb = 0; cb < kDC / 32; ++cb) O[cb] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.f;
-    for (;;) {  // one pass per reference choice; normally exactly one
-#pragma unroll
-      for (int cb = 0; cb < kDC / 32; ++cb) O[cb] = f32x16{};
-      l_run = 0.f;
-      bool redo = false;
-      if (threadIdx.x == 0) sm.redo = 0;
-      // page-table entry of the tile after next, fetched one iteration early
-      // so the lookup never sits on the critical path of a prefetch
-      int blk_next = ntiles > 1 ? pt[ulo + 1] : 0;
-      for (int it = 0; it < ntiles; ++it) {
-        const int u = ulo + it;
-        wait_vm();
-        __syncthreads();  // tile `it` landed for every wave; buffer (it+1)%2 is free
-        if (sm.redo) { redo = true; break; }
-        if (it + 1 < ntiles)
-          load_tile(sm.tile[(it + 1) & 1], block_at(__builtin_amdgcn_readfirstlane(blk_next)),
-                    valid_in(u + 1), wave, loff);
-        if (it + 2 < ntiles) blk_next = pt[u + 2];
-        const unsigned char* tb = sm.tile[it & 1];
-        const int nv = valid_in(u);
+    bf16x8 p_prev[2] = {}, p_cur[2];  // P of the step before the first: zero
 
-        // ---- S^T = K . Q^T  (two 32-token blocks, interleaved) ----
-        // Step n = 2*s + bt reads the K fragment of channel step s for token
-        // block bt (token 32*bt + hl sits in sub-block row 4*bt + hl/8, i.e.
-        // +36 KB per bt).  A 4-deep ring keeps 3 LDS reads in flight behind
-        // each MFMA; sched_barrier pins that order.
-        f32x16 S[2];
-        auto kaddr = [&](int n) {
-          const int s_ = n >> 1, bt = n & 1;
-          return tb + koff[s_ & 3] + (s_ >> 2) * 1024 + bt * 36864;
-        };
-        constexpr int kQK = 2 * (kD / 16);  // 72 MFMAs
-        bf16x8 kr[4];
+    // One pipeline step.  QK: S^T = K . Q^T for step h (36 MFMAs).  PV: O^T +=
+    // V^T . P^T for step h-1 (32 MFMAs), with the softmax of step h spread
+    // between them, so the exp/max VALU work runs under matrix work.  The
+    // first step has no PV yet; the drain after the last step has no QK.
+    auto run_step = [&](auto qk_on, auto pv_on, int h) __attribute__((always_inline)) {
+      constexpr bool kQKOn = decltype(qk_on)::value, kPVOn = decltype(pv_on)::value;
+      const uint32_t kb = lds_addr(sm.buf[h % kNBuf]) + koff0;
+      const uint32_t vb = lds_addr(sm.buf[h > 0 ? (h + kNBuf - 1) % kNBuf : 0]) + voff0;
+      auto kfrag = [&](int n) __attribute__((always_inline)) {  // chunk pair n&3 of sub-block column n>>2
+        return lds_b128_at((kb ^ uint32_t((n & 3) << 5)) + uint32_t((n >> 2) * 1024));
+      };
+      auto vfrag = [&](int n) __attribute__((always_inline)) {
+        const int i = n >> 4, cb = n & 15;
+        const uint32_t base = uint32_t((2 * i) * 9216 + (cb >> 1) * 1024);  // token rows 16i..16i+15
+        const uint32_t v = vb ^ uint32_t((cb & 1) << 6);
+        return lds_tr_pair_at(v + base, (v ^ 32u) + base + 9216u);
+      };
+      f32x16 S;
+      bf16x8 vr[kRV];
+      if constexpr (kQKOn) {
+        bf16x8 kr[kRK];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) kr[n] = lds_b128(kaddr(n));
+        for (int n = 0; n < kRK; ++n) kr[n] = kfrag(n);
 #pragma unroll
         for (int n = 0; n < kQK; ++n) {
-          const int s_ = n >> 1, bt = n & 1;
-          if (s_ == 0)
-            mfma_qk_first(S[bt], kr[n & 3], qf[s_]);
+          if (n == 0)
+            mfma_qk_first(S, kr[0], qf[0]);
           else
-            mfma_qk(S[bt], kr[n & 3], qf[s_]);
-          if (n + 4 < kQK) kr[n & 3] = lds_b128(kaddr(n + 4));
+            mfma_qk(S, kr[n % kRK], qf[n]);
+          if (n + kRK < kQK) {
+            kr[n % kRK] = kfrag(n + kRK);
+          } else if constexpr (kPVOn) {  // the tail of QK prefetches the first V fragments
+            const int v = n + kRK - kQK;
+            if (v < kRV) vr[v] = vfrag(v);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
-        scores_ready(S[0], S[1]);
+      } else {
+#pragma unroll
+        for (int n = 0; n < kRV; ++n) vr[n] = vfrag(n);
+      }
 
-        // ---- softmax (lane = one head; 32 of the 64 tokens) ----
-        if (nv < kBS) {  // partial last tile: mask tokens >= nv
-          const int lim = nv - 4 * g;
+      // softmax of step h in pieces (lane = one head; tokens 8*(r/4) + 4*g + r%4)
+      const int nv = kQKOn ? valid_in(h) : kStep;
+      float mx = 0.f, lsum = 0.f, corr = 1.f;
+      bool spike = false;
+      auto softmax_part = [&](int k) __attribute__((always_inline)) {
+        if constexpr (kQKOn) {
+          if (k == 0) scores_ready(S);
+          if (k == 1 && nv < kStep) {  // past-length tokens of a partial step: -inf
+            const int lim = nv - 4 * g;
 #pragma unroll
-          for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (32 * bt + 8 * (r / 4) + (r % 4) >= lim) S[bt][r] = -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[bt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c_log2;
-        if (m_ref == -INFINITY) m_ref = mx;  // first tile of the piece
-        if (__any(mx > m_ref + kHeadroom)) {
-          m_ref = fmaxf(m_ref, mx);
-          sm.redo = 1;  // seen by every wave after the next barrier
-          continue;
-        }
-        bf16x8 pf[4];
-        float lsum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(S[i / 2][8 * (i % 2) + e], c_log2, -m_ref));
-            lsum += p;
-            pf[i][e] = (__bf16)p;
+            for (int r = 0; r < 16; ++r) S[r] = (8 * (r / 4) + (r % 4) >= lim) ? -INFINITY : S[r];
           }
-        l_run += lsum;
-
-        // ---- O += P . V  (consecutive MFMAs update different O blocks) ----
-        // Step n = 16*i + cb: token step i, channel block cb; V fragments come
-        // from two transposed reads, kept 3 steps ahead in a 4-deep ring.
-        auto vfrag = [&](int n) {
-          const int i = n >> 4, cb = n & 15;
-          const int base = (2 * i) * 9216 + (cb >> 1) * 1024;  // voff[1] adds row 2i+1
-          return lds_tr_pair(tb + base + voff[0][cb & 1], tb + base + voff[1][cb & 1]);
-        };
-        constexpr int kPV = 4 * (kDC / 32);  // 64 MFMAs
-        bf16x8 vr[4];
+          if (k == 2) {
+            mx = S[0];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) vr[n] = vfrag(n);
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+          }
+          if (k == 3) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c_log2;
+            // the piece's first step sets the head's reference; a later step
+            // more than kHeadroom above it moves it (and rescales O below)
+            spike = m_ref != -INFINITY && mx > m_ref + kHeadroom;
+            const float m_new = m_ref == -INFINITY || spike ? mx : m_ref;
+            corr = spike ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+            m_ref = m_new;
+          }
+          if (k >= 4 && k < 12) {
+            const int i = (k - 4) >> 2, e0 = 2 * ((k - 4) & 3);
+#pragma unroll
+            for (int e = e0; e < e0 + 2; ++e) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_log2, -m_ref));
+              lsum += p;
+              p_cur[i][e] = (__bf16)p;
+            }
+          }
+        }
+      };
+
+      if constexpr (kPVOn) {
 #pragma unroll
         for (int n = 0; n < kPV; ++n) {
-          // O^T[channel][head] += V^T . P^T: the lane keeps one head, so the
-          // normalisation and the partial store need no cross-lane traffic
-          O[n & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[n & 3], pf[n >> 4], O[n & 15], 0, 0, 0);
-          if (n + 4 < kPV) vr[n & 3] = vfrag(n + 4);
+          mfma_pv(O[n & 15], vr[n % kRV], p_prev[n >> 4]);
+          if (n + kRV < kPV) vr[n % kRV] = vfrag(n + kRV);
+          softmax_part(n);
           __builtin_amdgcn_sched_barrier(0);
         }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 12; ++k) softmax_part(k);
       }
-      if (!redo) {
-        __syncthreads();
-        if (!sm.redo) break;  // a wave may have flagged on the very last tile
+      if constexpr (kQKOn) {
+        if (__any(spike)) {  // rare: rescale this wave's accumulated output
+          o_ready(O);
+#pragma unroll
+          for (int cb = 0; cb < kDC / 32; ++cb) {
+            O[cb] *= corr;                        // through VGPRs ...
+            asm volatile("" : "+a"(O[cb]));       // ... and back into the AGPRs
+          }
+        }
+        l_run = l_run * corr + lsum;
+        p_prev[0] = p_cur[0];
+        p_prev[1] = p_cur[1];
       }
-      // recompute the piece with the raised references
-      wait_vm();
-      __syncthreads();
-      load_tile(sm.tile[0], block_ptr(ulo), valid_in(ulo), wave, loff);
+    };
+
+    if (nsteps > 1) load_step(sm.buf[1], step_at(blk0, 1), valid_in(1), wave, loff);
+    // block of the next step to prefetch, looked up one step early
+    int blk_nx = nsteps > 2 ? pt[ulo + 1] : 0;
+    // Step h waits until its own loads are done (at most the loads of step
+    // h+1, issued one iteration earlier, still pending), then a barrier makes
+    // every wave's share visible and frees buffer (h+2)%4 for the next load.
+    auto begin_step = [&](int h) __attribute__((always_inline)) {
+      if (h + 1 < nsteps)
+        wait_vm<kLoadsPerWave>();
+      else
+        wait_vm<0>();
+      step_barrier();
+      if (h + 2 < nsteps)
+        load_step(sm.buf[(h + 2) % kNBuf], step_at(blk_nx, h + 2), valid_in(h + 2), wave, loff);
+      if (h + 3 < nsteps) blk_nx = pt[ulo + ((h + 3) >> 1)];
+    };
+    // Step 0 runs the same code with P = 0 against its own (finite, zero-filled
+    // past the length) buffer: a second specialisation without PV costs the
+    // register allocator more than these 32 MFMAs cost the piece.
+    for (int h = 0; h < nsteps; ++h) {
+      begin_step(h);
+      run_step(std::true_type{}, std::true_type{}, h);
     }
-    __syncthreads();  // buffers are reused by the next piece
+    run_step(std::false_type{}, std::true_type{}, nsteps);  // PV of the last step
+    o_ready(O);
+    __syncthreads();  // buffers are reused by the epilogue stage
 
     // ---- epilogue: normalise and write the partial (bf16) ----
-    // lane (g, hl) holds O^T rows = channels 32*cb + 8*rg + 4*g + {0..3} of head hl
+    // lane (g, hl) holds O^T rows = channels 32*cb + 8*rg + 4*g + {0..3} of
+    // head hl.  The wave first transposes its 32 x 512 block through the (now
+    // idle) step buffers, so that each global store covers one whole 1 KB head
+    // row; the stores are non-temporal.  Scattered or ordinary stores issued
+    // right after a piece has streamed through L2 run at a fraction of the
+    // write bandwidth, and nothing rereads the partials soon.
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
     if (lane < 32) a.ws_lse[orow0 + lane] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
-    uint16_t* orow = static_cast<uint16_t*>(a.ws_o) + (orow0 + hl) * kDC + 4 * g;
+    unsigned char* stage = &sm.buf[0][0] + wave * (32 * kStageRow);
 #pragma unroll
     for (int cb = 0; cb < kDC / 32; ++cb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const uint32_t lo = uint32_t(f32_to_bf16(O[cb][4 * rg + 0] * inv)) |
-                            (uint32_t(f32_to_bf16(O[cb][4 * rg + 1] * inv)) << 16);
-        const uint32_t hi = uint32_t(f32_to_bf16(O[cb][4 * rg + 2] * inv)) |
-                            (uint32_t(f32_to_bf16(O[cb][4 * rg + 3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(orow + 32 * cb + 8 * rg) = uint2{lo, hi};
+        const uint32_t lo = pack_bf16x2(O[cb][4 * rg + 0] * inv, O[cb][4 * rg + 1] * inv);
+        const uint32_t hi = pack_bf16x2(O[cb][4 * rg + 2] * inv, O[cb][4 * rg + 3] * inv);
+        *reinterpret_cast<uint2*>(stage + hl * kStageRow + (32 * cb + 8 * rg + 4 * g) * 2) = uint2{lo, hi};
       }
+    // the wave reads back only what it wrote itself: LDS order within a wave suffices
+    u32x4* orow = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws_o) + orow0 * kDC) + lane;
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + r * kStageRow + lane * 16),
+                                  orow + r * (kDC / 8));
+    step_barrier();  // every wave is done with the stage before a next piece loads into it
   });
 }
 

@@ -3,8 +3,8 @@
 //  * append: [c ; k^R] rows = h . [W^DKV ; W^KR]^T as split-K partials, then a
 //    per-token finalize (sum of partials, RoPE on k^R, cast, paged write,
 //    optional e4m3 tile quantisation)  ([MLA-93] Core Mechanics 1 and 3;
-//    decoding listing STEP 1);
-//  * out_proj: o[r, i, :] = W^UV_i u[r, i, :]  (decoding listing STEP 5).
+//    decoding section);
+//  * out_proj: o[r, i, :] = W^UV_i u[r, i, :]  ([MLA-93] decoding section).
 // Both are bound by streaming the weights once.  Operands go straight from
 // global memory into the MFMA lane layout (16 contiguous bytes per lane along
 // the reduction), so no LDS staging is needed.

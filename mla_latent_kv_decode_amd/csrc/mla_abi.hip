@@ -171,7 +171,9 @@ int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t
 
 size_t mla_decode_workspace_size(const mla_dims* d, int32_t batch, int32_t n_q,
                                  int32_t num_partitions) {
-  if (!d || batch < 0 || n_q < 1 || d->num_heads < 1 || d->d_latent < 1) return 0;
+  if (!d || batch < 0 || n_q < 1 || d->num_heads < 1 || d->d_latent < 1 ||
+      num_partitions > MLA_MAX_PARTITIONS)
+    return 0;
   const int G = num_partitions > 0 ? num_partitions : default_partitions(n_q);
   return ws_layout(d, batch, n_q, G).total;
 }
@@ -181,9 +183,9 @@ int mla_decode(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, con
                const int32_t* seq_lens, int32_t num_partitions, void* workspace,
                size_t workspace_bytes, mla_stream_t stream) {
   if (int e = check_dims(d, true)) return e;
-  if (batch < 0 || n_q < 1 || max_blocks_per_seq < 1)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d max_blocks_per_seq=%d", batch, n_q,
-                max_blocks_per_seq);
+  if (batch < 0 || n_q < 1 || max_blocks_per_seq < 1 || num_partitions > MLA_MAX_PARTITIONS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d max_blocks_per_seq=%d num_partitions=%d",
+                batch, n_q, max_blocks_per_seq, num_partitions);
   if (batch == 0) return ok();
   if (!q || !cache || !page_table || !seq_lens || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
@@ -233,7 +235,9 @@ int mla_decode_combine(const mla_dims* d, const void* workspace, size_t workspac
                        int32_t batch, int32_t n_q, const int32_t* seq_lens, int32_t num_partitions,
                        void* u_out, float* lse_out, mla_stream_t stream) {
   if (int e = check_dims(d, false)) return e;
-  if (batch < 0 || n_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d", batch, n_q);
+  if (batch < 0 || n_q < 1 || num_partitions > MLA_MAX_PARTITIONS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d num_partitions=%d", batch, n_q,
+                num_partitions);
   if (batch == 0) return ok();
   if (!workspace || !seq_lens || !u_out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if (!aligned(workspace, 256) || !aligned(u_out, elem_bytes(d->act_dtype)) || !aligned(seq_lens, 4) ||

@@ -7,6 +7,7 @@
 #include "../../include/mla.h"
 
 #define MLA_DEV static __device__ __forceinline__
+#define MLA_HD __host__ __device__ __forceinline__
 
 namespace mla {
 
@@ -23,6 +24,14 @@ MLA_DEV uint16_t f32_to_bf16(float x) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return uint16_t(u >> 16);
+}
+
+// Two floats to packed bf16 (round to nearest even) with the gfx950
+// conversion instruction.
+MLA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // OCP E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; S.1111.111 = NaN;
@@ -119,6 +128,31 @@ MLA_DEV int block_excl_scan(int v, int* red, int* total) {
   return base + incl - v;
 }
 
+// Two independent exclusive scans for the price of one pair of barriers;
+// red holds 2 * NT / 64 ints.
+template <int NT>
+MLA_DEV int2 block_excl_scan2(int va, int vb, int* red, int* tota, int* totb) {
+  const int l = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  int ia = va, ib = vb;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int ta = __shfl_up(ia, o, 64), tb = __shfl_up(ib, o, 64);
+    if (l >= o) { ia += ta; ib += tb; }
+  }
+  __syncthreads();
+  if (l == kWave - 1) { red[w] = ia; red[NT / kWave + w] = ib; }
+  __syncthreads();
+  int ba = 0, bb = 0, sa = 0, sb = 0;
+  for (int i = 0; i < NT / kWave; ++i) {
+    const int ra = red[i], rb = red[NT / kWave + i];
+    if (i < w) { ba += ra; bb += rb; }
+    sa += ra;
+    sb += rb;
+  }
+  *tota = sa;
+  *totb = sb;
+  return int2{ba + ia - va, bb + ib - vb};
+}
+
 // ---------------------------------------------------------------------------
 // Partition plan.
 //
@@ -130,73 +164,114 @@ MLA_DEV int block_excl_scan(int v, int* red, int* total) {
 // B + G - 1 of them.  G is first clamped to T so that no partition is empty
 // (an empty partition inside a sequence's span would own a slot it never
 // writes).  Every kernel recomputes this from seq_lens, so no planning launch
-// or stored plan is needed.
+// or stored plan is needed; with B <= NT it costs one load of seq_lens and two
+// workgroup scans.
 // ---------------------------------------------------------------------------
-MLA_DEV int64_t part_lo(int g, int64_t T, int G) { return (int64_t(g) * T) / G; }
-MLA_DEV int part_of_unit(int64_t u, int64_t T, int G) {
-  return int(((u + 1) * int64_t(G) - 1) / T);
+// floor(num / den) for 0 <= num < 2^52, den > 0: a double division (exact
+// enough at these magnitudes that the quotient is off by at most one) and an
+// integer correction.  Far shorter code than a 64-bit integer division.
+MLA_HD int64_t floor_div(int64_t num, int64_t den) {
+  int64_t q = int64_t(double(num) / double(den));
+  if (q * den > num) --q;
+  else if ((q + 1) * den <= num) ++q;
+  return q;
 }
+// Partitions of T units into G ranges (T < 2^31 and G <= 2^20, which the
+// host enforces, keep every product below 2^52).
+struct PartGrid {
+  int64_t T;
+  int G;
+  MLA_HD PartGrid(int64_t T_, int G_) : T(T_), G(G_) {}
+  MLA_HD int64_t lo(int g) const { return floor_div(int64_t(g) * T, G); }
+  MLA_HD int part_of(int64_t u) const {  // partition that owns unit u
+    return int(floor_div((u + 1) * int64_t(G) - 1, T));
+  }
+};
 MLA_DEV int units_of(int len, int bs) { return len <= 0 ? 0 : (len + bs - 1) / bs; }
 
 template <int NT>
 struct PlanScratch {
-  int S[NT], P[NT], n[NT], first[NT];
-  int red[NT / kWave];
+  // pieces of this partition in the current chunk of sequences
+  int b[NT], ulo[NT], uhi[NT], slot[NT], len[NT];
+  int red[2 * NT / kWave];
 };
 
+// T = total units.  Also returns the first chunk's per-thread length,
+// exclusive unit prefix and unit total, which the callers reuse (the whole
+// plan when B <= NT).
 template <int NT>
-MLA_DEV int plan_total_units(const int32_t* seq_lens, int B, int bs, PlanScratch<NT>& sc) {
+MLA_DEV int plan_total_units(const int32_t* seq_lens, int B, int bs, PlanScratch<NT>& sc, int* len0,
+                             int* S0, int* tot0) {
   int T = 0;
+  *len0 = *S0 = *tot0 = 0;
   for (int c = 0; c < B; c += NT) {
     const int b = c + threadIdx.x;
-    int n = b < B ? units_of(seq_lens[b], bs) : 0;
+    const int len = b < B ? seq_lens[b] : 0;
     int tot;
-    block_excl_scan<NT>(n, sc.red, &tot);
+    const int S = block_excl_scan<NT>(units_of(len, bs), sc.red, &tot);
+    if (c == 0) { *len0 = len; *S0 = S; *tot0 = tot; }
     T += tot;
   }
   return T;
 }
 
-// Calls f(b, unit_lo, unit_hi, slot) (units relative to the sequence start)
-// for every piece of partition g, in sequence order.  All threads call it
-// with identical arguments; f may use __syncthreads.
+// One chunk of sequences [c, c + NT): writes the pieces of partition g that
+// fall in it to sc (in sequence order) and returns their number.  len/S are
+// this thread's sequence length and global unit prefix; totP receives the
+// chunk's piece total.
+template <int NT>
+MLA_DEV int plan_chunk(int c, int len, int S, int bs, const PartGrid& pg, int g, int64_t lo,
+                       int64_t hi, int carryP, PlanScratch<NT>& sc, int* totP) {
+  const int n = units_of(len, bs);
+  const int first = n > 0 ? pg.part_of(S) : 0;
+  const int pieces = n > 0 ? pg.part_of(int64_t(S) + n - 1) - first + 1 : 0;
+  const bool mine = n > 0 && S < hi && int64_t(S) + n > lo;  // sequence meets [lo, hi)
+  int cnt;
+  const int2 r = block_excl_scan2<NT>(pieces, mine ? 1 : 0, sc.red, totP, &cnt);
+  if (mine) {
+    sc.b[r.y] = c + int(threadIdx.x);
+    sc.ulo[r.y] = int(max(lo, int64_t(S)) - S);
+    sc.uhi[r.y] = int(min(hi, int64_t(S) + n) - S);
+    sc.slot[r.y] = carryP + r.x + (g - first);
+    sc.len[r.y] = len;
+  }
+  __syncthreads();
+  return cnt;
+}
+
+// Calls f(b, unit_lo, unit_hi, slot, seq_len) (units relative to the
+// sequence start) for every piece of partition g, in sequence order.  All
+// threads call it with identical arguments; f may use __syncthreads.  Only
+// workgroup-uniform values stay live across f (the chunk-0 list is built
+// before the loop), so f gets the whole register file.
 template <int NT, class F>
 MLA_DEV void plan_for_each_piece(const int32_t* seq_lens, int B, int bs, int G, int g,
                                  PlanScratch<NT>& sc, F&& f) {
-  const int T = plan_total_units<NT>(seq_lens, B, bs, sc);
+  int len0, S0, tot0;
+  const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
   if (T == 0) return;
   G = min(G, T);
   if (g >= G) return;
-  const int64_t lo = part_lo(g, T, G), hi = part_lo(g + 1, T, G);
+  const PartGrid pg(T, G);
+  const int64_t lo = pg.lo(g), hi = pg.lo(g + 1);
   if (lo >= hi) return;
-  int carryS = 0, carryP = 0;
-  for (int c = 0; c < B; c += NT) {
-    const int b = c + threadIdx.x;
-    const int n = b < B ? units_of(seq_lens[b], bs) : 0;
-    int totN, totP;
-    const int S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
-    const int first = n > 0 ? part_of_unit(S, T, G) : 0;
-    const int pieces = n > 0 ? part_of_unit(int64_t(S) + n - 1, T, G) - first + 1 : 0;
-    const int P = carryP + block_excl_scan<NT>(pieces, sc.red, &totP);
-    sc.S[threadIdx.x] = S;
-    sc.P[threadIdx.x] = P;
-    sc.n[threadIdx.x] = n;
-    sc.first[threadIdx.x] = first;
-    __syncthreads();
-    const int cnt = min(NT, B - c);
-    bool done = false;
-    for (int k = 0; k < cnt; ++k) {
-      const int Sk = sc.S[k], nk = sc.n[k];
-      if (Sk >= hi) { done = true; break; }
-      if (int64_t(Sk) + nk <= lo || nk == 0) continue;
-      const int ulo = int(max(lo, int64_t(Sk)) - Sk);
-      const int uhi = int(min(hi, int64_t(Sk) + nk) - Sk);
-      f(c + k, ulo, uhi, sc.P[k] + (g - sc.first[k]));
-    }
-    __syncthreads();
-    if (done) return;
-    carryS += totN;
-    carryP += totP;
+  int totP;
+  int cnt = plan_chunk<NT>(0, len0, S0, bs, pg, g, lo, hi, 0, sc, &totP);
+  int c = 0, carryS = 0, carryP = 0, totN = tot0;
+  for (;;) {
+    cnt = __builtin_amdgcn_readfirstlane(cnt);
+    for (int k = 0; k < cnt; ++k)
+      f(sc.b[k], sc.ulo[k], sc.uhi[k], sc.slot[k], sc.len[k]);
+    if (c + NT >= B || carryS + totN >= hi) return;
+    carryS = __builtin_amdgcn_readfirstlane(carryS + totN);
+    carryP = __builtin_amdgcn_readfirstlane(carryP + totP);
+    c += NT;
+    __syncthreads();  // the next chunk rewrites the piece list
+    const int b = c + int(threadIdx.x);
+    const int len = b < B ? seq_lens[b] : 0;
+    const int S = carryS + block_excl_scan<NT>(units_of(len, bs), sc.red, &totN);
+    totN = __builtin_amdgcn_readfirstlane(totN);
+    cnt = plan_chunk<NT>(c, len, S, bs, pg, g, lo, hi, carryP, sc, &totP);
   }
 }
 
@@ -204,29 +279,33 @@ MLA_DEV void plan_for_each_piece(const int32_t* seq_lens, int B, int bs, int G, 
 template <int NT>
 MLA_DEV void plan_lookup(const int32_t* seq_lens, int B, int bs, int G, int b,
                          PlanScratch<NT>& sc, int* slot0, int* npieces) {
-  const int T = plan_total_units<NT>(seq_lens, B, bs, sc);
+  int len0, S0, tot0;
+  const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
   *slot0 = 0;
   *npieces = 0;
   if (T == 0) return;
   G = min(G, T);
+  const PartGrid pg(T, G);
   int carryS = 0, carryP = 0;
   for (int c = 0; c <= b; c += NT) {
     const int bb = c + threadIdx.x;
-    const int n = bb < B ? units_of(seq_lens[bb], bs) : 0;
-    int totN, totP;
-    const int S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
-    const int first = n > 0 ? part_of_unit(S, T, G) : 0;
-    const int pieces = n > 0 ? part_of_unit(int64_t(S) + n - 1, T, G) - first + 1 : 0;
+    int n = units_of(len0, bs), S = S0, totN = tot0;
+    if (c > 0) {
+      n = bb < B ? units_of(seq_lens[bb], bs) : 0;
+      S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
+    }
+    const int first = n > 0 ? pg.part_of(S) : 0;
+    const int pieces = n > 0 ? pg.part_of(int64_t(S) + n - 1) - first + 1 : 0;
+    int totP;
     const int P = carryP + block_excl_scan<NT>(pieces, sc.red, &totP);
-    __syncthreads();
     if (bb == b) {
-      sc.S[0] = P;
-      sc.n[0] = pieces;
+      sc.b[0] = P;
+      sc.ulo[0] = pieces;
     }
     __syncthreads();
     if (b < c + NT) {
-      *slot0 = sc.S[0];
-      *npieces = sc.n[0];
+      *slot0 = sc.b[0];
+      *npieces = sc.ulo[0];
       __syncthreads();
       return;
     }

@@ -1,5 +1,5 @@
 // Per-head value up-projection o[r, i, :] = W^UV_i u[r, i, :]
-// ([MLA-93] decoding listing STEP 5).  Generic VALU path: one workgroup per
+// ([MLA-93] decoding section).  Generic VALU path: one workgroup per
 // (head, 16-row tile, 128-wide d_v tile), reduction chunks staged in LDS.
 #include "mla_internal.h"
 

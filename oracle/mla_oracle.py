@@ -152,7 +152,7 @@ def dequantize_fp8_rows(codes, scales) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# RoPE ([MLA-93] decode listing, apply_rope; Core Mechanics 2 and 3)
+# RoPE ([MLA-93] Core Mechanics 2 and 3, and the rotation used in its decoding section)
 # --------------------------------------------------------------------------
 
 def rope_angles(n: int, pos: float, base: float = 10000.0) -> np.ndarray:
@@ -182,7 +182,7 @@ def rope(x, pos, base: float = 10000.0) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# cache append ([MLA-93] Core Mechanics 1 and 3; decode listing STEP 1)
+# cache append ([MLA-93] Core Mechanics 1 and 3; decoding section)
 # --------------------------------------------------------------------------
 
 def kv_rows(h, w_dkv, w_kr, positions, base: float = 10000.0) -> np.ndarray:
@@ -253,7 +253,7 @@ def gather_sequence(pool: dict, page_table, b: int, length: int, block_size: int
 
 def softmax_scale(d_nope: int, d_rope: int) -> float:
     """1 / sqrt(d_nope + d_R): the per-head key is 192-wide for DeepSeek dims
-    ([MLA-93] Core Mechanics 3 and the decode listing's scale)."""
+    ([MLA-93] Core Mechanics 3 and the scale its decoding section uses)."""
     return 1.0 / math.sqrt(d_nope + d_rope)
 
 
@@ -406,7 +406,7 @@ def combine(o_parts, lse_parts):
 
 
 # --------------------------------------------------------------------------
-# per-head value up-projection ([MLA-93] decode listing STEP 5)
+# per-head value up-projection ([MLA-93] decoding section)
 # --------------------------------------------------------------------------
 
 def out_proj(u, w_uv) -> np.ndarray:
@@ -417,7 +417,7 @@ def out_proj(u, w_uv) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# query side ([MLA-93] decode listing STEPs 2-3; Core Mechanics 3)
+# query side ([MLA-93] decoding section and Core Mechanics 3)
 # --------------------------------------------------------------------------
 
 def split_query(qfull, n_heads: int, d_nope: int, d_rope: int):

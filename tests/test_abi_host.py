@@ -70,6 +70,9 @@ def test_decode_validation_errors(L):
     bad = _dims(L, act_dtype=L.FP8_E4M3)
     assert call(ctypes.byref(bad)) == L.ERR_INVALID_ARGUMENT
     assert call(ctypes.byref(d), batch=0) == L.OK                       # nothing to do
+    assert call(ctypes.byref(d), G=(1 << 20) + 1) == L.ERR_INVALID_ARGUMENT  # partition cap
+    assert L.mla_decode_workspace_size(d, 4, 1, (1 << 20) + 1) == 0
+    assert L.mla_decode_workspace_size(d, 4, 1, 1 << 20) > 0
     big = _dims(L, d_latent=1024, flags=L.FLAG_GENERIC_DECODE)
     ws_big = L.mla_decode_workspace_size(big, 4, 1, 8)
     assert lib.mla_decode(ctypes.byref(big), FAKE, 4, 1, FAKE, None, FAKE, 16, FAKE, 8, FAKE,
@@ -94,6 +97,8 @@ def test_other_entry_points_validate(L):
         == L.ERR_WORKSPACE_TOO_SMALL
     assert lib.mla_decode_combine(ctypes.byref(d), None, 10, 4, 1, FAKE, 8, FAKE, None, None) \
         == L.ERR_INVALID_ARGUMENT
+    assert lib.mla_decode_combine(ctypes.byref(d), FAKE, 1 << 40, 4, 1, FAKE, (1 << 20) + 1, FAKE,
+                                  None, None) == L.ERR_INVALID_ARGUMENT
     assert lib.mla_out_proj(ctypes.byref(d), FAKE, -1, FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT
     assert lib.mla_out_proj(ctypes.byref(d), None, 4, FAKE, FAKE, None) == L.ERR_INVALID_ARGUMENT
     assert lib.mla_out_proj(ctypes.byref(d), FAKE, 0, FAKE, FAKE, None) == L.OK

@@ -302,6 +302,20 @@ def test_full_size_sampled(name):
 
 
 # --------------------------------------------------------------------------
+# more sequences than one plan chunk (a workgroup scans 256 sequences at a time)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("generic", [False, True])
+@pytest.mark.parametrize("G", [1, 300, 700])
+def test_decode_many_sequences(generic, G):
+    import mla_latent_kv_decode_amd as M
+    cfg = W.scaled(W.CONFIGS["ragged"], batch=300, len_lo=1, len_hi=160)
+    case = DecodeCase(cfg)
+    u, lse = case.run(flags=M.FLAG_GENERIC_DECODE if generic else 0, G=G)
+    compare_sampled(case, u, lse, [0, 1, 128, 255, 256, 257, 299])
+    assert torch.isfinite(u.float()).all()
+
+
+# --------------------------------------------------------------------------
 # the MFMA decode kernel (default path for H=128, d_c=512, d_R=64, bf16)
 # --------------------------------------------------------------------------
 MFMA_SMALL = [
