@@ -10,6 +10,10 @@ Default workload: DeepSeek-V3 shape, bf16, B=64 sequences of L=4096 cached
 tokens, one query token each, H=128, d_c=512, d_R=64, block 64, shuffled page
 table.  Inputs are resident in HBM before timing; several copies of the pool
 are rotated so the 256 MB last-level cache cannot serve the cache stream.
+The timed region launches the four calls per step with only a start and a
+stop event (--graph replays one captured HIP graph per step instead); the
+per-kernel times, and the decode time the roofline uses, come from a second
+pass of the same steps with an event around every call.
 
 Prints one JSON line (rank 0).  Metric: KV-tokens/s = sum_b L_b per step / time.
 """
@@ -43,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--generic", action="store_true", help="force the generic decode kernel")
+    p.add_argument("--graph", action="store_true",
+                   help="capture each step (per pool copy) into one HIP graph and replay it")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (5 times), to "
                         "scale HBM byte counters; prints nothing else")
@@ -144,35 +150,68 @@ def main():
     o = torch.empty(B * n_q, H, d.d_v, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    # The four calls of a step, each a closure over one pool copy.
+    def calls(i):
         pool, sc = pools[i % n_copies], scales[i % n_copies]
-        if ev: ev[0].record(stream)
-        M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc, aws)
-        if ev: ev[1].record(stream)
-        M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G)
-        if ev: ev[2].record(stream)
-        M.mla_decode_combine(dims, ws, lens_t, u, None, G)
-        if ev: ev[3].record(stream)
-        M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o)
-        if ev: ev[4].record(stream)
+        return [
+            lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc, aws),
+            lambda: M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G),
+            lambda: M.mla_decode_combine(dims, ws, lens_t, u, None, G),
+            lambda: M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o),
+        ]
 
     for i in range(args.warmup):
-        step(i)
+        for c in calls(i):
+            c()
     torch.cuda.synchronize()
 
+    # --graph: the four calls of a step (per pool copy) are captured once into
+    # one HIP graph (they allocate nothing and record no memsets) and a step
+    # replays it.  Default: the calls are launched directly.
+    if args.graph:
+        cap = torch.cuda.Stream()
+        runners = []
+        for i in range(n_copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for c in calls(i):
+                    c()
+            runners.append(g.replay)
+        for i in range(args.warmup):
+            runners[i % n_copies]()
+        torch.cuda.synchronize()
+        run_step = lambda i: runners[i % n_copies]()
+    else:
+        def run_step(i):
+            for c in calls(i):
+                c()
+
     # ---- timed region: exactly K steps ------------------------------------
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # Only a start and a stop event: an event recorded between two kernels
+    # costs the stream several microseconds, so per-kernel times come from a
+    # second, separately timed pass below.
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        run_step(i)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
+
+    # ---- per-kernel times: K more steps with an event around every call ----
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev = evs[i]
+        for k, c in enumerate(calls(i)):
+            ev[k].record(stream)
+            c()
+        ev[4].record(stream)
+    torch.cuda.synchronize()
     per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
     k_ms = per.mean(axis=0)
     decode_ms = float(k_ms[1])
@@ -214,6 +253,7 @@ def main():
         "kernels_ms": {"append": round(float(k_ms[0]), 5), "decode": round(decode_ms, 5),
                        "combine": round(float(k_ms[2]), 5), "out_proj": round(float(k_ms[3]), 5)},
         "decode_kernel": "generic" if args.generic else "default",
+        "launch": "hip_graph_replay" if args.graph else "direct",
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -367,3 +367,63 @@ def test_decode_mfma_score_spike_in_late_tile():
     u, lse = case.run(G=1)
     compare_sampled(case, u, lse, [0, 1])
     assert float(lse[0, 0, 0]) > 30.0
+
+
+# --------------------------------------------------------------------------
+# the step captured into HIP graphs (how bench.py and a serving loop run it)
+# --------------------------------------------------------------------------
+def test_graph_replay_matches_eager():
+    """append + decode + combine + out_proj captured as HIP graphs and replayed
+    three times, with eager work on the stream between replays: every replay
+    reproduces the eager outputs bit for bit (the calls allocate nothing and
+    record no memsets, so they are safe to capture)."""
+    import mla_latent_kv_decode_amd as M
+    cfg = W.scaled(W.CONFIGS["ragged"], batch=6, len_lo=40, len_hi=900)
+    case = DecodeCase(cfg)
+    d = case.d
+    B, n_q, H = case.q.shape[0], case.q.shape[1], d.num_heads
+    dims = dims_of(cfg)
+    G = 16
+    dev = "cuda"
+    ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, G), dtype=torch.uint8, device=dev)
+    u = torch.empty(B, n_q, H, d.d_latent, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, n_q, H, dtype=torch.float32, device=dev)
+    o = torch.empty(B * n_q, H, d.d_v, dtype=torch.bfloat16, device=dev)
+    w_uv = W.normal((H, d.d_v, d.d_latent), 41, std=1 / math.sqrt(d.d_latent), device=dev,
+                    dtype=torch.bfloat16)
+    T = B * n_q  # the n_q newest tokens of every sequence are rewritten by append
+    h = W.normal((T, d.d_model), 42, device=dev, dtype=torch.bfloat16)
+    w_dkv = W.weight(d.d_latent, d.d_model, 43, dtype=torch.bfloat16, device=dev)
+    w_kr = W.weight(d.d_rope, d.d_model, 44, dtype=torch.bfloat16, device=dev)
+    seq_ids = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(n_q)
+    positions = (case.lens_t.repeat_interleave(n_q) - n_q
+                 + torch.arange(n_q, dtype=torch.int32, device=dev).repeat(B)).to(torch.int32)
+    aws = append_workspace(dims, T, d.d_model)
+    calls = [
+        lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, case.table_t,
+                                   case.pool, None, aws),
+        lambda: M.mla_decode(dims, case.q, case.pool, None, case.table_t, case.lens_t, ws, G),
+        lambda: M.mla_decode_combine(dims, ws, case.lens_t, u, lse, G),
+        lambda: M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o),
+    ]
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    ref = [bits(x).clone() for x in (u, lse, o, case.pool)]
+    assert torch.isfinite(o.float()).all()
+    cap = torch.cuda.Stream()
+    graphs = []
+    for c in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            c()
+        graphs.append(g)
+    for rep in range(3):
+        for x in (u, lse, o, ws):
+            x.zero_()  # eager work between replays
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((u, lse, o, case.pool), ref):
+            assert torch.equal(bits(got), want), f"replay {rep} differs from the eager run"
