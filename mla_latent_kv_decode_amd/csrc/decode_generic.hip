@@ -142,95 +142,129 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the pieces of each (sequence, query token, head):
 // M = max_s lse_s, w_s = exp(lse_s - M), u = sum_s w_s o_s / sum_s w_s,
-// lse = M + ln sum_s w_s.  One workgroup per (b, j) and group of 4 heads;
-// 64 threads per head, each owning 8 consecutive channels (two float4).
+// lse = M + ln sum_s w_s.  One workgroup per (b, j) and 16 heads; a wave owns
+// 4 heads, a lane 8 consecutive channels of each (16 bytes of bf16 / 32 of
+// fp32).  Pieces are merged in chunks of 4 with a running maximum; a chunk's
+// lse values and partial rows are all loaded before any of them is used, so
+// the wave waits for memory once per chunk.
 // ---------------------------------------------------------------------------
 constexpr int kCombNT = 256;
-constexpr int kCombHeads = kCombNT / 64;
-constexpr int kCombChunk = 64;  // pieces weighed per pass
+constexpr int kCHW = 4;                        // heads per wave
+constexpr int kCPC = 4;                        // pieces per chunk
+constexpr int kCombHeads = kCombNT / kWave * kCHW;  // heads per workgroup
 
+// 8 consecutive channels of a partial row, kept as loaded (bf16 pairs or fp32)
 template <int ADT>
+struct Raw8 {
+  uint4 w[ADT == MLA_FP32 ? 2 : 1];
+  __device__ __forceinline__ void load(const void* base, size_t off) {
+    if constexpr (ADT == MLA_FP32) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
+      w[0] = src[0];
+      w[1] = src[1];
+    } else {
+      w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    }
+  }
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (ADT == MLA_FP32) {
+      const uint4& q = w[e / 4];
+      const uint32_t v = (e % 4) == 0 ? q.x : (e % 4) == 1 ? q.y : (e % 4) == 2 ? q.z : q.w;
+      return __uint_as_float(v);
+    } else {
+      const uint32_t v = (e / 2) == 0 ? w[0].x : (e / 2) == 1 ? w[0].y : (e / 2) == 2 ? w[0].z : w[0].w;
+      return __uint_as_float((e % 2) == 0 ? v << 16 : v & 0xffff0000u);
+    }
+  }
+};
+
+// NV = 8-channel vectors per lane (d_latent <= 512 * NV)
+template <int ADT, int NV>
 __global__ __launch_bounds__(kCombNT) void combine_kernel(CombineArgs a) {
   __shared__ PlanScratch<kCombNT> plan;
-  __shared__ float wts[kCombHeads][kCombChunk];
   const int bj = blockIdx.x;
   const int b = bj / a.n_q, j = bj % a.n_q;
-  const int hh = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int h = blockIdx.y * kCombHeads + hh;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   int slot0, np;
   plan_lookup<kCombNT>(a.seq_lens, a.batch, a.block_size, a.G, b, plan, &slot0, &np);
-  const int H = a.H, dc = a.d_latent;
-  const bool live = h < H;
-  const size_t orow = (size_t(b) * a.n_q + j) * H + (live ? h : 0);
-  auto lse_of = [&](int s) { return a.ws_lse[(size_t(slot0 + s) * a.n_q + j) * H + h]; };
-  // global max over the pieces (one wave per head)
-  float M = -INFINITY;
-  if (live)
-    for (int s = lane; s < np; s += 64) M = fmaxf(M, lse_of(s));
-  M = wave_max(M);
-  float wsum = 0.f;
-  // channels of this thread: 8 per chunk of 512
-  const int nvec = dc / 8;  // threads needed per head
-  float acc[2][8];
-  for (int r = 0; r < 2; ++r)
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
-  for (int s0 = 0; s0 < np; s0 += kCombChunk) {
-    const int cnt = min(kCombChunk, np - s0);
-    float w = 0.f;
-    if (live && lane < cnt) {
-      const float ls = lse_of(s0 + lane);
-      w = ls == -INFINITY ? 0.f : expf(ls - M);
-    }
-    wsum += wave_sum(w);
-    __syncthreads();
-    wts[hh][lane] = w;
-    __syncthreads();
-    if (live) {
-      for (int r = 0; r < 2; ++r) {
-        const int v = lane + 64 * r;  // float8 index within the row
-        if (v >= nvec) break;
-#pragma unroll 4
-        for (int s = 0; s < cnt; ++s) {
-          const float ws_ = wts[hh][s];
-          const size_t off = ((size_t(slot0 + s0 + s) * a.n_q + j) * H + h) * dc + 8 * v;
-          float x[8];
-          if constexpr (ADT == MLA_FP32) {
-            const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.ws_o) + off);
-            const float4 x0 = src[0], x1 = src[1];
-            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-          } else {
-            const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.ws_o) + off);
-            const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  const int H = a.H, dc = a.d_latent, nvec = dc / 8;
+  const int h0 = blockIdx.y * kCombHeads + w * kCHW;
+  float M[kCHW], wsum[kCHW], acc[kCHW][NV][8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[2 * e] = __uint_as_float(wv[e] << 16);
-              x[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
-            }
-          }
+  for (int k = 0; k < kCHW; ++k) {
+    M[k] = -INFINITY;
+    wsum[k] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[r][e] += ws_ * x[e];
+    for (int r = 0; r < NV; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[k][r][e] = 0.f;
+  }
+  for (int s0 = 0; s0 < np; s0 += kCPC) {
+    const int cnt = min(kCPC, np - s0);
+    float ls[kCHW][kCPC];
+    Raw8<ADT> x[kCHW][kCPC][NV];
+#pragma unroll
+    for (int k = 0; k < kCHW; ++k)
+#pragma unroll
+      for (int s = 0; s < kCPC; ++s) {
+        ls[k][s] = -INFINITY;
+        if (s < cnt && h0 + k < H) {
+          const size_t r = (size_t(slot0 + s0 + s) * a.n_q + j) * H + h0 + k;
+          ls[k][s] = a.ws_lse[r];
+#pragma unroll
+          for (int rr = 0; rr < NV; ++rr)
+            if (lane + 64 * rr < nvec) x[k][s][rr].load(a.ws_o, r * dc + 8 * (lane + 64 * rr));
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < kCHW; ++k) {
+      float mc = ls[k][0];
+#pragma unroll
+      for (int s = 1; s < kCPC; ++s) mc = fmaxf(mc, ls[k][s]);
+      const float Mn = fmaxf(M[k], mc);
+      const float sc = M[k] == -INFINITY ? 0.f : expf(M[k] - Mn);  // rescale earlier chunks
+      M[k] = Mn;
+      wsum[k] *= sc;
+#pragma unroll
+      for (int rr = 0; rr < NV; ++rr)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][rr][e] *= sc;
+#pragma unroll
+      for (int s = 0; s < kCPC; ++s) {
+        const float ws_ = ls[k][s] == -INFINITY ? 0.f : expf(ls[k][s] - Mn);
+        wsum[k] += ws_;
+        if (ws_ != 0.f) {
+#pragma unroll
+          for (int rr = 0; rr < NV; ++rr)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[k][rr][e] += ws_ * x[k][s][rr].get(e);
         }
       }
     }
   }
-  if (!live) return;
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int r = 0; r < 2; ++r) {
-    const int v = lane + 64 * r;
-    if (v >= nvec) break;
-    if constexpr (ADT == MLA_FP32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.u) + orow * dc + 8 * v);
-      dst[0] = float4{acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv};
-      dst[1] = float4{acc[r][4] * inv, acc[r][5] * inv, acc[r][6] * inv, acc[r][7] * inv};
-    } else {
-      uint32_t pk[4];
-      for (int e = 0; e < 4; ++e)
-        pk[e] = uint32_t(f32_to_bf16(acc[r][2 * e] * inv)) | (uint32_t(f32_to_bf16(acc[r][2 * e + 1] * inv)) << 16);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.u) + orow * dc + 8 * v) = uint4{pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+  for (int k = 0; k < kCHW; ++k) {
+    const int h = h0 + k;
+    if (h >= H) break;
+    const size_t orow = (size_t(b) * a.n_q + j) * H + h;
+    const float inv = wsum[k] > 0.f ? 1.f / wsum[k] : 0.f;
+#pragma unroll
+    for (int rr = 0; rr < NV; ++rr) {
+      const int v = lane + 64 * rr;
+      if (v >= nvec) break;
+      if constexpr (ADT == MLA_FP32) {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.u) + orow * dc + 8 * v);
+        dst[0] = float4{acc[k][rr][0] * inv, acc[k][rr][1] * inv, acc[k][rr][2] * inv, acc[k][rr][3] * inv};
+        dst[1] = float4{acc[k][rr][4] * inv, acc[k][rr][5] * inv, acc[k][rr][6] * inv, acc[k][rr][7] * inv};
+      } else {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(acc[k][rr][2 * e] * inv, acc[k][rr][2 * e + 1] * inv);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.u) + orow * dc + 8 * v) = uint4{pk[0], pk[1], pk[2], pk[3]};
+      }
     }
+    if (lane == 0 && a.lse_out) a.lse_out[orow] = wsum[k] > 0.f ? M[k] + logf(wsum[k]) : -INFINITY;
   }
-  if (lane == 0 && a.lse_out) a.lse_out[orow] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
 bool combine_vector_ok(const CombineArgs& a) { return a.d_latent % 8 == 0 && a.d_latent <= 1024; }
@@ -276,10 +310,14 @@ __global__ __launch_bounds__(kCombNT) void combine_scalar_kernel(CombineArgs a) 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   if (combine_vector_ok(a)) {
     dim3 grid(unsigned(a.batch) * a.n_q, unsigned((a.H + kCombHeads - 1) / kCombHeads));
-    if (a.act_dtype == MLA_FP32)
-      hipLaunchKernelGGL(combine_kernel<MLA_FP32>, grid, dim3(kCombNT), 0, st, a);
-    else
-      hipLaunchKernelGGL(combine_kernel<MLA_BF16>, grid, dim3(kCombNT), 0, st, a);
+    const bool two = a.d_latent > 512;
+    if (a.act_dtype == MLA_FP32) {
+      if (two) hipLaunchKernelGGL((combine_kernel<MLA_FP32, 2>), grid, dim3(kCombNT), 0, st, a);
+      else hipLaunchKernelGGL((combine_kernel<MLA_FP32, 1>), grid, dim3(kCombNT), 0, st, a);
+    } else {
+      if (two) hipLaunchKernelGGL((combine_kernel<MLA_BF16, 2>), grid, dim3(kCombNT), 0, st, a);
+      else hipLaunchKernelGGL((combine_kernel<MLA_BF16, 1>), grid, dim3(kCombNT), 0, st, a);
+    }
   } else {
     dim3 grid(unsigned(a.batch) * a.n_q, unsigned(a.H));
     if (a.act_dtype == MLA_FP32)

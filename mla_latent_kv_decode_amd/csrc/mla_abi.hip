@@ -108,10 +108,11 @@ mla::AppendArgs append_args(const mla_dims* d, int32_t n_tokens, int32_t d_model
   a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
   return a;
 }
-// The matrix-core append applies to bf16 activations (pointer alignment is
-// checked again at call time).
+// The matrix-core append applies to bf16 activations with the RoPE part inside
+// one 128-channel tile (pointer alignment is checked again at call time).
 bool append_uses_mfma(const mla::AppendArgs& a) {
-  return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024 && a.D % 4 == 0;
+  return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024 && a.D % 4 == 0 &&
+         (a.d_rope == 0 || a.d_latent / 128 == (a.D - 1) / 128);
 }
 }  // namespace
 
