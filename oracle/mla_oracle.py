@@ -17,8 +17,7 @@ Sources (page titles; sections named on each page):
             2 (RoPE non-commutativity), 3 (decoupled RoPE and matrix
             absorption); "Total Cached Scalars per Token"; the section
             "Production PyTorch Implementation: Single-Token MLA Decoding"
-            (its apply_rope helper and the five numbered steps of its decode
-            function).
+            (the rotation it applies and its decoding procedure).
 * [V3-ARCH] "DeepSeek-V3 Architecture: Multi-Head Latent Attention (MLA) &
             FP8 Mixed-Precision Training" -- 1 "The Memory Wall",
             2 "MLA Mathematics", A "Decoupled RoPE", 3 "Matrix Absorption".
