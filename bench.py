@@ -4,8 +4,10 @@
 A step is one pass of the whole hot path on one batch of synthetic input:
   mla_cache_append  (B new tokens: W^DKV / W^KR projection, RoPE, paged write)
   mla_decode        (split-KV attention over the latent cache, all heads)
-  mla_decode_combine(log-sum-exp merge of the splits)
-  mla_out_proj      (per-head W^UV up-projection)
+  mla_decode_combine_out_proj
+                    (log-sum-exp merge of the splits, then the per-head W^UV
+                     up-projection, in one kernel; --separate runs
+                     mla_decode_combine and mla_out_proj as two calls)
 Default workload: DeepSeek-V3 shape, bf16, B=64 sequences of L=4096 cached
 tokens, one query token each, H=128, d_c=512, d_R=64, block 64, shuffled page
 table.  Inputs are resident in HBM before timing; several copies of the pool
@@ -47,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--generic", action="store_true", help="force the generic decode kernel")
+    p.add_argument("--separate", action="store_true",
+                   help="run mla_decode_combine and mla_out_proj as two calls instead of the "
+                        "fused mla_decode_combine_out_proj")
     p.add_argument("--graph", action="store_true",
                    help="capture each step (per pool copy) into one HIP graph and replay it")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -150,15 +155,21 @@ def main():
     o = torch.empty(B * n_q, H, d.d_v, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    # The four calls of a step, each a closure over one pool copy.
+    # The calls of a step, each a closure over one pool copy.
     def calls(i):
         pool, sc = pools[i % n_copies], scales[i % n_copies]
-        return [
+        head = [
             lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc, aws),
             lambda: M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G),
-            lambda: M.mla_decode_combine(dims, ws, lens_t, u, None, G),
-            lambda: M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o),
         ]
+        if args.separate:
+            return head + [
+                lambda: M.mla_decode_combine(dims, ws, lens_t, u, None, G),
+                lambda: M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o),
+            ]
+        return head + [lambda: M.mla_decode_combine_out_proj(dims, ws, lens_t, w_uv, o, B, n_q, None,
+                                                             None, G)]
+    names = ["append", "decode"] + (["combine", "out_proj"] if args.separate else ["combine_out_proj"])
 
     for i in range(args.warmup):
         for c in calls(i):
@@ -203,16 +214,17 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # ---- per-kernel times: K more steps with an event around every call ----
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    nk = len(names)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         ev = evs[i]
         for k, c in enumerate(calls(i)):
             ev[k].record(stream)
             c()
-        ev[4].record(stream)
+        ev[nk].record(stream)
     torch.cuda.synchronize()
-    per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
+    per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
     k_ms = per.mean(axis=0)
     decode_ms = float(k_ms[1])
 
@@ -250,8 +262,7 @@ def main():
                                f"cache={cfg.cache_dtype}",
                    "batch": B, "kv_tokens_per_step": kv_tokens, "n_q": n_q,
                    "partitions": G, "pool_copies_rotated": n_copies},
-        "kernels_ms": {"append": round(float(k_ms[0]), 5), "decode": round(decode_ms, 5),
-                       "combine": round(float(k_ms[2]), 5), "out_proj": round(float(k_ms[3]), 5)},
+        "kernels_ms": {n: round(float(t), 5) for n, t in zip(names, k_ms)},
         "decode_kernel": "generic" if args.generic else "default",
         "launch": "hip_graph_replay" if args.graph else "direct",
         "wall_s_timed": round(wall, 4),

@@ -183,6 +183,30 @@ int mla_decode_combine(const mla_dims *dims, const void *workspace, size_t works
 int mla_out_proj(const mla_dims *dims, const void *u, int32_t rows, const void *w_uv, void *out,
                  mla_stream_t stream);
 
+/*
+ * mla_decode_combine_out_proj -- mla_decode_combine followed by mla_out_proj
+ * in one pass, so the merged latent output u need not round-trip through
+ * memory: per row r = b * n_q + j and head i,
+ *   u = sum_s w_s o_s / sum_s w_s (as mla_decode_combine, rounded to the
+ *   activation dtype), then out[r][i] = W^UV_i u ([MLA-93] decoding section).
+ * Arguments as in the two calls it replaces:
+ *   workspace / workspace_bytes / batch / n_q / seq_lens / num_partitions:
+ *            exactly those of the preceding mla_decode;
+ *   w_uv     [num_heads][d_v][d_latent] act_dtype;
+ *   out      [batch * n_q][num_heads][d_v] act_dtype;
+ *   u_out    [batch][n_q][num_heads][d_latent] act_dtype, or NULL (u is then
+ *            not stored);
+ *   lse_out  [batch][n_q][num_heads] fp32, or NULL.
+ * The fused kernel covers bf16 activations with d_latent = 512 and d_v a
+ * multiple of 32 up to 128; other shapes run the two separate kernels, which
+ * needs u_out (else MLA_ERR_UNSUPPORTED).
+ */
+int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
+                                size_t workspace_bytes, int32_t batch, int32_t n_q,
+                                const int32_t *seq_lens, int32_t num_partitions,
+                                const void *w_uv, void *out, void *u_out, float *lse_out,
+                                mla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

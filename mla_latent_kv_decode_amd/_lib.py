@@ -26,7 +26,8 @@ ERR_HIP = -4
 
 EXPORTS = ("mla_abi_version", "mla_last_error", "mla_device_cu_count",
            "mla_cache_append_workspace_size", "mla_cache_append",
-           "mla_decode_workspace_size", "mla_decode", "mla_decode_combine", "mla_out_proj")
+           "mla_decode_workspace_size", "mla_decode", "mla_decode_combine", "mla_out_proj",
+           "mla_decode_combine_out_proj")
 
 
 class MlaError(RuntimeError):
@@ -83,7 +84,10 @@ def lib():
         L.mla_decode.argtypes = [D, _P, _I, _I, _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P]
         L.mla_decode_combine.argtypes = [D, _P, ctypes.c_size_t, _I, _I, _P, _I, _P, _P, _P]
         L.mla_out_proj.argtypes = [D, _P, _I, _P, _P, _P]
-        for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj"):
+        L.mla_decode_combine_out_proj.argtypes = [D, _P, ctypes.c_size_t, _I, _I, _P, _I, _P, _P,
+                                                  _P, _P, _P]
+        for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj",
+                  "mla_decode_combine_out_proj"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -152,6 +156,16 @@ def mla_decode_combine(dims, workspace, seq_lens, u_out, lse_out=None, num_parti
                                     workspace.numel() * workspace.element_size(),
                                     u_out.shape[0], u_out.shape[1], _ptr(seq_lens),
                                     num_partitions, _ptr(u_out), _ptr(lse_out), _stream(stream)))
+
+
+def mla_decode_combine_out_proj(dims, workspace, seq_lens, w_uv, out, batch: int, n_q: int,
+                                u_out=None, lse_out=None, num_partitions: int = 0, stream=None):
+    """out [B*n_q, H, d_v]; u_out [B, n_q, H, d_latent] or None; lse_out [B, n_q, H] or None."""
+    _check(lib().mla_decode_combine_out_proj(ctypes.byref(dims), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             batch, n_q, _ptr(seq_lens), num_partitions,
+                                             _ptr(w_uv), _ptr(out), _ptr(u_out), _ptr(lse_out),
+                                             _stream(stream)))
 
 
 def mla_out_proj(dims, u, w_uv, out, stream=None):

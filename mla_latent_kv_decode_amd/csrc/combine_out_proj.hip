@@ -1,0 +1,254 @@
+// Log-sum-exp merge of the decode partials followed by the per-head value
+// up-projection, in one pass: for every row r = (b, j) and head i,
+//   u = sum_s w_s o_s / sum_s w_s,  w_s = exp(lse_s - max_s lse_s)
+//   o[r, i, :] = W^UV_i u
+// ([MLA-93] decoding section: attention output aggregated in latent space,
+// then up-projected by W^UV).  u never has to leave the chip.
+//
+// One workgroup per (head, 32 rows); d_latent = 512, d_v <= 128 (multiple of
+// 32), bf16 partials and weights, fp32 accumulation.
+//  * The head's W^UV_i (d_v rows of 1 KB) is copied into LDS first, one direct
+//    1 KB load per row with the 16-byte chunks XOR-swizzled by row; it streams
+//    in while the workgroup merges the partials.
+//  * Each wave merges 8 rows: every lane owns 8 channels; the lse values and
+//    partial rows of a chunk of 4 pieces are loaded for all 8 rows before any
+//    is used.  The merged u row is rounded to bf16 (as mla_decode_combine
+//    stores it) and written to an LDS tile with the same swizzle.
+//  * Wave w then computes output columns 32w..32w+31 with 32
+//    v_mfma_f32_32x32x16_bf16 (A = u rows, B = W rows, both from LDS).
+//  * Workgroup ids are remapped so the row groups of one head run on one XCD
+//    and share its L2 for W^UV_i.
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+constexpr int kNT = 256;
+constexpr int kRows = 32;                 // rows per workgroup
+constexpr int kRowsPerWave = kRows / (kNT / kWave);
+constexpr int kDC = 512;
+constexpr int kRowBytes = kDC * 2;        // one 1 KB row of u or W
+constexpr int kMaxDV = 128;
+constexpr int kPC = 4;                    // pieces merged per chunk
+
+struct Smem {
+  alignas(128) unsigned char w[kMaxDV * kRowBytes];  // W^UV_i
+  alignas(128) unsigned char u[kRows * kRowBytes];   // merged rows (bf16)
+};
+// the plan scratch and slot tables live in the u tile until it is written
+constexpr int kMaxSeq = kRows + 1;
+static_assert(sizeof(PlanScratch<kNT>) + 2 * kMaxSeq * sizeof(int) <= kRows * kRowBytes,
+              "plan scratch must fit the u tile");
+
+MLA_DEV uint32_t lds_addr(const unsigned char* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const lds_u8*)p));
+}
+// byte offset of 16-byte chunk c of row `row` (chunks XOR-swizzled by row)
+MLA_DEV uint32_t chunk_off(int row, int c) { return uint32_t(row * kRowBytes + ((c ^ (row & 15)) << 4)); }
+
+__global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void combine_out_proj_kernel(CombineProjArgs a) {
+  extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane / 32, m = lane % 32;
+  const int R = a.batch * a.n_q, H = a.H, dv = a.d_v;
+  const int ngroups = (R + kRows - 1) / kRows;
+  // consecutive logical ids share an XCD (workgroups are dealt round-robin)
+  const int NB = gridDim.x, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;
+  const int h = logical / ngroups, r0 = (logical % ngroups) * kRows;
+  const int nrows = min(kRows, R - r0);
+
+  // W^UV_i -> LDS: dv/4 rows per wave, one 1 KB direct load each.  Issued
+  // after the first chunk's partial loads: vector-memory operations complete
+  // in order, so waiting for those loads then never waits for W.
+  auto load_w = [&]() {
+    const unsigned char* wsrc = static_cast<const unsigned char*>(a.w_uv) + size_t(h) * dv * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wsrc, (short)0, dv * kRowBytes, 0x00020000);
+    const int per = dv / (kNT / kWave);
+    for (int i = 0; i < per; ++i) {
+      const int row = wave * per + i;
+      // lane l fills LDS chunk slot l of the row with source chunk l ^ (row & 15)
+      const uint32_t voff = uint32_t((lane ^ (row & 15)) << 4);
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                   :
+                   : "v"(voff), "s"(rs), "s"(row * kRowBytes), "{m0}"(lds_addr(sm.w + row * kRowBytes))
+                   : "memory");
+    }
+  };
+
+  // ---- 1. first slot and piece count of this group's sequences ----
+  PlanScratch<kNT>& ps = *reinterpret_cast<PlanScratch<kNT>*>(sm.u);
+  int* t_slot0 = reinterpret_cast<int*>(sm.u + sizeof(PlanScratch<kNT>));
+  int* t_np = t_slot0 + kMaxSeq;
+  const int b_lo = r0 / a.n_q;
+  const int nb = (r0 + nrows - 1) / a.n_q - b_lo + 1;
+  plan_slots<kNT>(a.seq_lens, a.batch, a.block_size, a.G, b_lo, nb, ps, t_slot0, t_np);
+  int slot0[kRowsPerWave], np[kRowsPerWave], maxnp = 0;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = wave * kRowsPerWave + i;
+    slot0[i] = 0;
+    np[i] = 0;
+    if (r < nrows) {
+      const int bi = (r0 + r) / a.n_q - b_lo;
+      slot0[i] = __builtin_amdgcn_readfirstlane(t_slot0[bi]);
+      np[i] = __builtin_amdgcn_readfirstlane(t_np[bi]);
+      maxnp = max(maxnp, np[i]);
+    }
+  }
+  __syncthreads();  // the tables are read; the u tile may be overwritten
+
+  // ---- 2. merge the pieces of this wave's 8 rows (lane = 8 channels) ----
+  float M[kRowsPerWave], wsum[kRowsPerWave], acc[kRowsPerWave][8];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    M[i] = -INFINITY;
+    wsum[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+  }
+  // per row: the lse / partial row of its first piece; pieces of one
+  // (sequence, query) are n_q * H rows apart
+  const size_t pstride = size_t(a.n_q) * H;
+  const float* lrow[kRowsPerWave];
+  const uint16_t* orow_ws[kRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int j = (r0 + wave * kRowsPerWave + i) % a.n_q;
+    const size_t r = (size_t(slot0[i]) * a.n_q + j) * H + h;
+    lrow[i] = a.ws_lse + r;
+    orow_ws[i] = static_cast<const uint16_t*>(a.ws_o) + r * kDC + 8 * lane;
+  }
+  if (maxnp == 0) load_w();  // no pieces at all (then u is zero)
+  for (int s0 = 0; s0 < maxnp; s0 += kPC) {
+    float ls[kRowsPerWave][kPC];
+    uint4 x[kRowsPerWave][kPC];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+      for (int s = 0; s < kPC; ++s) {
+        // Loads are unconditional (a branch around each would make the wave
+        // wait for every load before issuing the next): a piece past the
+        // row's count reads the row's last piece (a row with none reads
+        // slot 0) and is masked below by lse = -inf.
+        const int p = max(0, min(s0 + s, np[i] - 1));
+        const size_t off = size_t(p) * pstride;
+        ls[i][s] = lrow[i][np[i] > 0 ? off : 0];
+        x[i][s] = *reinterpret_cast<const uint4*>(orow_ws[i] + (np[i] > 0 ? off * kDC : 0));
+      }
+    if (s0 == 0) load_w();
+    __builtin_amdgcn_sched_barrier(0);  // every load of the chunk is issued before the first use
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+      for (int s = 0; s < kPC; ++s)
+        if (s0 + s >= np[i]) ls[i][s] = -INFINITY;  // mask pieces past the row's count
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      float mc = ls[i][0];
+#pragma unroll
+      for (int s = 1; s < kPC; ++s) mc = fmaxf(mc, ls[i][s]);
+      const float Mn = fmaxf(M[i], mc);
+      const float sc = M[i] == -INFINITY ? 0.f : expf(M[i] - Mn);  // rescale earlier chunks
+      M[i] = Mn;
+      wsum[i] *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i][e] *= sc;
+#pragma unroll
+      for (int s = 0; s < kPC; ++s) {
+        const float w = ls[i][s] == -INFINITY ? 0.f : expf(ls[i][s] - Mn);
+        wsum[i] += w;
+        if (w != 0.f) {
+          const uint32_t v[4] = {x[i][s].x, x[i][s].y, x[i][s].z, x[i][s].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[i][2 * e] += w * __uint_as_float(v[e] << 16);
+            acc[i][2 * e + 1] += w * __uint_as_float(v[e] & 0xffff0000u);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = wave * kRowsPerWave + i;
+    const float inv = wsum[i] > 0.f ? 1.f / wsum[i] : 0.f;
+    uint4 pk;
+    pk.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+    pk.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+    pk.z = pack_bf16x2(acc[i][4] * inv, acc[i][5] * inv);
+    pk.w = pack_bf16x2(acc[i][6] * inv, acc[i][7] * inv);
+    // rows past the end get zeros: they feed MFMA rows that are never stored
+    *reinterpret_cast<uint4*>(sm.u + chunk_off(r, lane)) = pk;
+    if (r < nrows) {
+      const size_t orow = size_t(r0 + r) * H + h;  // (b * n_q + j) * H + h
+      if (a.u) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.u) + orow * kDC + 8 * lane) = pk;
+      if (a.lse_out && lane == 0) a.lse_out[orow] = wsum[i] > 0.f ? M[i] + logf(wsum[i]) : -INFINITY;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows have landed
+  __syncthreads();                                  // u tile and all W rows visible
+
+  // ---- 3. o[rows, h, 32w..32w+31] = u . W^T on MFMA ----
+  const int v0 = wave * 32;
+  if (v0 >= dv) return;
+  f32x16 o = {};
+  const uint32_t ub = lds_addr(sm.u), wb = lds_addr(sm.w);
+  auto afrag = [&](int s) { return *(lds_bf16x8*)(uintptr_t)(ub + chunk_off(m, 2 * s + g)); };
+  auto bfrag = [&](int s) { return *(lds_bf16x8*)(uintptr_t)(wb + chunk_off(v0 + m, 2 * s + g)); };
+  constexpr int kK = kDC / 16;
+  bf16x8 ar[4], br[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    ar[s] = afrag(s);
+    br[s] = bfrag(s);
+  }
+#pragma unroll
+  for (int s = 0; s < kK; ++s) {
+    o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[s & 3], br[s & 3], o, 0, 0, 0);
+    if (s + 4 < kK) {
+      ar[s & 3] = afrag(s + 4);
+      br[s & 3] = bfrag(s + 4);
+    }
+  }
+  // lane (g, m) holds rows 8*(k/4) + 4*g + k%4 of column v0 + m
+  __bf16* out = static_cast<__bf16*>(a.out);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = 8 * (k / 4) + 4 * g + (k % 4);
+    if (r < nrows) out[(size_t(r0 + r) * H + h) * dv + v0 + m] = (__bf16)o[k];
+  }
+}
+
+}  // namespace
+
+bool combine_out_proj_supported(const CombineProjArgs& a) {
+  return a.d_latent == kDC && a.d_v > 0 && a.d_v <= kMaxDV && a.d_v % 32 == 0 &&
+         (reinterpret_cast<uintptr_t>(a.w_uv) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.ws_o) % 16) == 0 &&
+         (a.u == nullptr || (reinterpret_cast<uintptr_t>(a.u) % 16) == 0);
+}
+
+hipError_t launch_combine_out_proj(const CombineProjArgs& a, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(combine_out_proj_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(Smem)));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int R = a.batch * a.n_q;
+  const unsigned n = unsigned(a.H) * unsigned((R + kRows - 1) / kRows);
+  hipLaunchKernelGGL(combine_out_proj_kernel, dim3(n), dim3(kNT), sizeof(Smem), st, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -207,15 +207,22 @@ __global__ __launch_bounds__(kCombNT) void combine_kernel(CombineArgs a) {
     for (int k = 0; k < kCHW; ++k)
 #pragma unroll
       for (int s = 0; s < kCPC; ++s) {
-        ls[k][s] = -INFINITY;
-        if (s < cnt && h0 + k < H) {
-          const size_t r = (size_t(slot0 + s0 + s) * a.n_q + j) * H + h0 + k;
-          ls[k][s] = a.ws_lse[r];
+        // unconditional loads from clamped (valid) rows, masked by lse = -inf:
+        // a branch around each load would serialise them
+        const bool live = s < cnt && h0 + k < H;
+        const size_t r = (size_t(slot0 + s0 + min(s, cnt - 1)) * a.n_q + j) * H + min(h0 + k, H - 1);
+        (void)live;
+        ls[k][s] = a.ws_lse[r];
 #pragma unroll
-          for (int rr = 0; rr < NV; ++rr)
-            if (lane + 64 * rr < nvec) x[k][s][rr].load(a.ws_o, r * dc + 8 * (lane + 64 * rr));
-        }
+        for (int rr = 0; rr < NV; ++rr)
+          x[k][s][rr].load(a.ws_o, r * dc + 8 * min(lane + 64 * rr, nvec - 1));
       }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the chunk is issued before the first use
+#pragma unroll
+    for (int k = 0; k < kCHW; ++k)
+#pragma unroll
+      for (int s = 0; s < kCPC; ++s)
+        if (!(s < cnt && h0 + k < H)) ls[k][s] = -INFINITY;  // mask clamped loads
 #pragma unroll
     for (int k = 0; k < kCHW; ++k) {
       float mc = ls[k][0];

@@ -292,3 +292,53 @@ int mla_out_proj(const mla_dims* d, const void* u, int32_t rows, const void* w_u
 }
 
 }  // extern "C"
+
+int mla_decode_combine_out_proj(const mla_dims* d, const void* workspace, size_t workspace_bytes,
+                                int32_t batch, int32_t n_q, const int32_t* seq_lens,
+                                int32_t num_partitions, const void* w_uv, void* out, void* u_out,
+                                float* lse_out, mla_stream_t stream) {
+  if (int e = check_dims(d, false)) return e;
+  if (batch < 0 || n_q < 1 || num_partitions > MLA_MAX_PARTITIONS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d num_partitions=%d", batch, n_q,
+                num_partitions);
+  if (batch == 0) return ok();
+  if (!workspace || !seq_lens || !w_uv || !out)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t ae = elem_bytes(d->act_dtype);
+  if (!aligned(workspace, 256) || !aligned(seq_lens, 4) || !aligned(w_uv, ae) || !aligned(out, ae) ||
+      (u_out && !aligned(u_out, ae)) || (lse_out && !aligned(lse_out, 4)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  const int G = num_partitions > 0 ? num_partitions : default_partitions(n_q);
+  const WsLayout w = ws_layout(d, batch, n_q, G);
+  if (workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes,
+                w.total);
+  mla::CombineProjArgs a;
+  a.ws_o = workspace;
+  a.ws_lse = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.lse_off);
+  a.seq_lens = seq_lens;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.u = u_out;
+  a.lse_out = lse_out;
+  a.batch = batch;
+  a.n_q = n_q;
+  a.H = d->num_heads;
+  a.d_latent = d->d_latent;
+  a.d_v = d->d_v;
+  a.block_size = d->block_size;
+  a.G = G;
+  hipError_t e;
+  if (d->act_dtype == MLA_BF16 && mla::combine_out_proj_supported(a)) {
+    e = mla::launch_combine_out_proj(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "combine_out_proj launch");
+    return ok();
+  }
+  if (!u_out)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "combine_out_proj: no fused kernel for these dims; pass u_out to run the two passes");
+  if (int r = mla_decode_combine(d, workspace, workspace_bytes, batch, n_q, seq_lens,
+                                 num_partitions, u_out, lse_out, stream))
+    return r;
+  return mla_out_proj(d, u_out, batch * n_q, w_uv, out, stream);
+}

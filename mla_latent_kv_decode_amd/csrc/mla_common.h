@@ -315,6 +315,44 @@ MLA_DEV void plan_lookup(const int32_t* seq_lens, int B, int bs, int G, int b,
   }
 }
 
+// First slot and piece count of every sequence in [b_lo, b_lo + nb), written
+// to t_slot0 / t_np (nb entries each, typically LDS).  All threads call it;
+// the tables are complete when it returns.
+template <int NT>
+MLA_DEV void plan_slots(const int32_t* seq_lens, int B, int bs, int G, int b_lo, int nb,
+                        PlanScratch<NT>& sc, int* t_slot0, int* t_np) {
+  for (int i = threadIdx.x; i < nb; i += NT) {
+    t_slot0[i] = 0;
+    t_np[i] = 0;
+  }
+  int len0, S0, tot0;
+  const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);  // barriers order the zeroing
+  if (T > 0) {
+    G = min(G, T);
+    const PartGrid pg(T, G);
+    int carryS = 0, carryP = 0;
+    for (int c = 0; c < B && c < b_lo + nb; c += NT) {
+      const int b = c + int(threadIdx.x);
+      int n = units_of(len0, bs), S = S0, totN = tot0;
+      if (c > 0) {
+        n = b < B ? units_of(seq_lens[b], bs) : 0;
+        S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
+      }
+      const int first = n > 0 ? pg.part_of(S) : 0;
+      const int pieces = n > 0 ? pg.part_of(int64_t(S) + n - 1) - first + 1 : 0;
+      int totP;
+      const int P = carryP + block_excl_scan<NT>(pieces, sc.red, &totP);
+      if (b >= b_lo && b < b_lo + nb && b < B) {
+        t_slot0[b - b_lo] = P;
+        t_np[b - b_lo] = pieces;
+      }
+      carryS += totN;
+      carryP += totP;
+    }
+  }
+  __syncthreads();
+}
+
 // Workspace layout: [o: n_slots][n_q][H][d_latent] in the activation dtype |
 // [lse: n_slots][n_q][H] fp32.
 struct Workspace {

@@ -28,6 +28,18 @@ struct CombineArgs {
   int act_dtype;
 };
 
+// combine + out_proj in one pass (d_latent = 512, bf16)
+struct CombineProjArgs {
+  const void* ws_o;        // bf16 partials
+  const float* ws_lse;
+  const int32_t* seq_lens;
+  const void* w_uv;        // [H][d_v][d_latent]
+  void* out;               // [B * n_q][H][d_v]
+  void* u;                 // [B][n_q][H][d_latent] or null
+  float* lse_out;          // [B][n_q][H] or null
+  int batch, n_q, H, d_latent, d_v, block_size, G;
+};
+
 struct AppendArgs {
   const void* h;           // [T][d_model]
   const void* w_dkv;       // [d_latent][d_model]
@@ -55,6 +67,8 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 bool decode_mfma_supported(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+bool combine_out_proj_supported(const CombineProjArgs& a);
+hipError_t launch_combine_out_proj(const CombineProjArgs& a, hipStream_t st);
 bool append_supported(const AppendArgs& a);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 bool append_mfma_supported(const AppendArgs& a);

@@ -113,3 +113,20 @@ def test_other_entry_points_validate(L):
     assert L.mla_cache_append_workspace_size(f32, 4, 64) == 0
     assert ap(ctypes.byref(f32), dm=64, ws=None, wsb=0) == L.ERR_UNSUPPORTED  # RoPE straddles tiles
     assert ap(ctypes.byref(d), T=0) == L.OK
+
+
+def test_combine_out_proj_validates(L):
+    lib = L.lib()
+    d = _dims(L)
+    ws = L.mla_decode_workspace_size(d, 4, 1, 8)
+    call = lambda dims, ws_ptr=FAKE, ws_bytes=ws, w=FAKE, out=FAKE, u=None, G=8: \
+        lib.mla_decode_combine_out_proj(dims, ws_ptr, ws_bytes, 4, 1, FAKE, G, w, out, u, None, None)
+    assert call(None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), ws_ptr=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), out=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), ws_bytes=ws - 1) == L.ERR_WORKSPACE_TOO_SMALL
+    assert call(ctypes.byref(d), G=(1 << 20) + 1) == L.ERR_INVALID_ARGUMENT
+    odd = _dims(L, d_v=100)  # no fused kernel for d_v % 32 != 0, and no u_out to fall back on
+    ws_odd = L.mla_decode_workspace_size(odd, 4, 1, 8)
+    assert call(ctypes.byref(odd), ws_bytes=ws_odd) == L.ERR_UNSUPPORTED
+    assert "u_out" in lib.mla_last_error().decode()

@@ -370,6 +370,57 @@ def test_decode_mfma_score_spike_in_late_tile():
 
 
 # --------------------------------------------------------------------------
+# combine + out_proj fused (the merged u stays on chip)
+# --------------------------------------------------------------------------
+FUSED = [
+    (W.scaled(W.CONFIGS["ragged"], batch=6, len_lo=40, len_hi=900), 16),   # 12 rows: one partial group
+    (W.scaled(W.CONFIGS["v3"], batch=40, seq_len=333), 0),                  # 40 rows: 32 + 8
+    (W.scaled(W.CONFIGS["ragged"], batch=5, len_lo=2, len_hi=3000), 64),    # up to ~30 pieces a row
+]
+
+
+@pytest.mark.parametrize("idx", range(len(FUSED)))
+def test_combine_out_proj_matches_separate_calls_and_oracle(idx):
+    import mla_latent_kv_decode_amd as M
+    cfg, G = FUSED[idx]
+    case = DecodeCase(cfg)
+    d = case.d
+    B, n_q, H = case.q.shape[0], case.q.shape[1], d.num_heads
+    dims = dims_of(cfg)
+    ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, G), dtype=torch.uint8, device="cuda")
+    M.mla_decode(dims, case.q, case.pool, None, case.table_t, case.lens_t, ws, G)
+    w_uv = W.normal((H, d.d_v, d.d_latent), 51, std=1 / math.sqrt(d.d_latent), device="cuda",
+                    dtype=torch.bfloat16)
+    # separate calls
+    u_s = torch.empty(B, n_q, H, d.d_latent, dtype=torch.bfloat16, device="cuda")
+    l_s = torch.empty(B, n_q, H, dtype=torch.float32, device="cuda")
+    o_s = torch.empty(B * n_q, H, d.d_v, dtype=torch.bfloat16, device="cuda")
+    M.mla_decode_combine(dims, ws, case.lens_t, u_s, l_s, G)
+    M.mla_out_proj(dims, u_s.view(B * n_q, H, d.d_latent), w_uv, o_s)
+    # fused, with and without storing u
+    u_f = torch.full_like(u_s, float("nan"))
+    l_f = torch.full_like(l_s, float("nan"))
+    o_f = torch.full_like(o_s, float("nan"))
+    o_f2 = torch.full_like(o_s, float("nan"))
+    M.mla_decode_combine_out_proj(dims, ws, case.lens_t, w_uv, o_f, B, n_q, u_f, l_f, G)
+    M.mla_decode_combine_out_proj(dims, ws, case.lens_t, w_uv, o_f2, B, n_q, None, None, G)
+    torch.cuda.synchronize()
+    # the merge is the same arithmetic in the same order: bit for bit
+    assert torch.equal(u_f.view(torch.int16), u_s.view(torch.int16))
+    assert torch.equal(l_f, l_s)
+    assert torch.equal(o_f.view(torch.int16), o_f2.view(torch.int16))
+    # the projection sums the 512 products in another order
+    assert rel_l2(to_f64(o_f), to_f64(o_s)) <= 2e-3
+    # and against the oracle
+    rows = list(range(B))
+    u_ref = np.stack([case.oracle(b)[0] for b in rows])
+    o_ref = O.out_proj(u_ref.reshape(B * n_q, H, d.d_latent), to_f64(w_uv))
+    got = to_f64(o_f)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, o_ref) <= 1e-2 and max_abs(got, o_ref) <= 2e-2
+
+
+# --------------------------------------------------------------------------
 # the step captured into HIP graphs (how bench.py and a serving loop run it)
 # --------------------------------------------------------------------------
 def test_graph_replay_matches_eager():
