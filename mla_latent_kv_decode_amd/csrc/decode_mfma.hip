@@ -58,14 +58,25 @@ constexpr int kStep = 32;                     // tokens per step
 constexpr int kRowBytes = kD * 2;             // 1152
 constexpr int kBlockBytes = kBS * kRowBytes;  // 73728
 constexpr int kStepBytes = kStep * kRowBytes; // 36864 = 36 sub-blocks of 1 KB
-constexpr int kNBuf = 4;                      // LDS step buffers: h-1 (PV), h (QK), h+1, h+2 in flight
+constexpr int kNBuf = 4;                      // bf16 cache: LDS step buffers h-1 (PV), h (QK), h+1, h+2 in flight
+// fp8 cache: three bf16 step buffers (h-1, h, h+1 being converted) and two
+// staging buffers for the e4m3 codes (18 KB) and scales (640 B, one 1 KB load)
+constexpr int kF8NBuf = 3;
+constexpr int kF8Codes = kStep * kD;                 // 18432
+constexpr int kF8ScaleBytes = kStep * 5 * 4;         // 640
+constexpr int kF8Stage = kF8Codes + 1024;            // 19456
+constexpr int kF8Loads = kF8Codes / 1024;            // 18 direct loads of codes per step
+constexpr int kLdsBytes = (kNBuf * kStepBytes > kF8NBuf * kStepBytes + 2 * kF8Stage)
+                              ? kNBuf * kStepBytes : kF8NBuf * kStepBytes + 2 * kF8Stage;
 constexpr int kLoadsPerWave = 9;              // 1 KB direct loads per wave per step
 constexpr float kHeadroom = 32.0f;            // log2 headroom above the reference max
 constexpr int kStageRow = kDC * 2 + 16;       // epilogue transpose row (padded against bank conflicts)
 constexpr int kQK = kD / 16;                  // score MFMAs per step
 constexpr int kPV = 2 * (kDC / 32);           // output MFMAs per step
 constexpr int kRK = 4, kRV = 4;               // LDS operand fragments read ahead of their MFMA
-static_assert(4 * 32 * kStageRow <= kNBuf * kStepBytes, "epilogue stage must fit the step buffers");
+static_assert(4 * 32 * kStageRow <= kLdsBytes, "epilogue stage must fit the step buffers");
+static_assert(kF8NBuf * kStepBytes + 2 * kF8Stage <= kLdsBytes && kF8ScaleBytes <= 1024, "fp8 staging layout");
+static_assert(kNT / kWave == kNBuf && kH * kRowBytes <= kLdsBytes, "Q is staged through the step buffers");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -83,7 +94,9 @@ MLA_DEV int step_off(int t, int c) {
 }
 
 struct Smem {
-  alignas(128) unsigned char buf[kNBuf][kStepBytes];  // kStepBytes is a multiple of 128
+  // bf16 step buffer i at i * kStepBytes (kStepBytes is a multiple of 128);
+  // for the fp8 cache, staging buffer i follows the three step buffers
+  alignas(128) unsigned char lds[kLdsBytes];
   PlanScratch<kNT> plan;
 };
 
@@ -138,12 +151,72 @@ MLA_DEV void load_step(unsigned char* dst, const unsigned char* src, int nvalid,
   load_all(r, dst, wave, loff, std::make_integer_sequence<int, kLoadsPerWave>{});
 }
 
+// One fp8 step into a staging buffer: the 32 rows of e4m3 codes are one
+// contiguous 18 KB run (18 direct 1 KB loads, dealt round-robin to the waves)
+// and their 32 x 5 fp32 scales one more load (wave 3, which has one code load
+// fewer).  The codes' descriptor covers only the live rows, so the rest reads
+// zeros; the scales are read whole (640 bytes, inside the block) and those of
+// rows past the length are dropped by the conversion.
+MLA_DEV void load_step_f8(unsigned char* dst, const unsigned char* codes, const float* scales,
+                          int nvalid, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, nvalid * kD, 0x00020000);
+  for (int k = wave; k < kF8Loads; k += kNT / kWave) {
+    const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(dst + k * 1024)));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(lane * 16), "s"(rc), "s"(k * 1024), "{m0}"(lds)
+                 : "memory");
+  }
+  if (wave == kNT / kWave - 1) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, kF8ScaleBytes, 0x00020000);
+    const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(dst + kF8Codes)));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(lane * 16), "s"(rs), "{m0}"(lds)
+                 : "memory");
+  }
+}
+
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 MLA_DEV uint32_t lds_addr(const unsigned char* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_u8*)p));
 }
 MLA_DEV bf16x8 lds_b128_at(uint32_t addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
+
+// Dequantise a staged fp8 step into a bf16 step buffer (the cache-step
+// layout): value = e4m3 code (decoded exactly) * its (token, 128-channel tile)
+// scale in fp32, rounded once to bf16.  Unit u = 16 codes of one token.
+// Rows at or past `nvalid` have zero codes; their scale is replaced by 0 so
+// whatever the cache holds there (NaN included) yields exact zeros.
+MLA_DEV void convert_step_f8(unsigned char* dst, const unsigned char* stage, int nvalid) {
+  typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+  typedef __attribute__((address_space(3))) u32x4 lds_u4w;
+  typedef __attribute__((address_space(3))) const float lds_f32;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const uint32_t sb = lds_addr(stage), db = lds_addr(dst);
+  for (int u = threadIdx.x; u < kStep * (kD / 16); u += kNT) {
+    const int t = u / (kD / 16), c8 = u % (kD / 16);
+    const u32x4 cw = *(lds_u4*)(uintptr_t)(sb + t * kD + c8 * 16);
+    const float sc_raw = *(lds_f32*)(uintptr_t)(sb + kF8Codes + (t * 5 + c8 / 8) * 4);
+    const float sc = t < nvalid ? sc_raw : 0.f;
+    const uint32_t w[4] = {cw[0], cw[1], cw[2], cw[3]};
+    uint32_t o[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[e]), false);  // codes 4e, 4e+1
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[e]), true);   // codes 4e+2, 4e+3
+      o[2 * e] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+      o[2 * e + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+    }
+    *(lds_u4w*)(uintptr_t)(db + step_off(t, 2 * c8)) = u32x4{o[0], o[1], o[2], o[3]};
+    *(lds_u4w*)(uintptr_t)(db + step_off(t, 2 * c8 + 1)) = u32x4{o[4], o[5], o[6], o[7]};
+  }
+}
 
 MLA_DEV bf16x8 lds_tr_pair_at(uint32_t p0, uint32_t p1) {
   i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
@@ -182,10 +255,16 @@ MLA_DEV void o_ready(f32x16 (&O)[16]) {
                  "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
 }
 
+template <bool kF8>
 __global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  constexpr int NB = kF8 ? kF8NBuf : kNBuf;  // bf16 step buffers in the ring
+  auto bbuf = [&](int i) __attribute__((always_inline)) { return sm.lds + i * kStepBytes; };
+  auto stage_buf = [&](int i) __attribute__((always_inline)) {
+    return sm.lds + kF8NBuf * kStepBytes + i * kF8Stage;
+  };
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -237,20 +316,39 @@ void decode_mfma_kernel(DecodeArgs a) {
     auto step_at = [&](int blk, int h) {  // first byte of step h, which lies in block blk
       return cache + int64_t(blk) * kBlockBytes + (h & 1) * kStepBytes;
     };
+    // fp8 cache: 1-byte codes, rows of kD bytes; scales [blk][64][5]
+    auto load_f8 = [&](int i, int blk, int h, int nvalid) __attribute__((always_inline)) {
+      load_step_f8(stage_buf(i), cache + int64_t(blk) * (kBS * kD) + (h & 1) * kF8Codes,
+                   a.scales + (int64_t(blk) * kBS + (h & 1) * kStep) * 5, nvalid, wave, lane);
+    };
     auto valid_in = [&](int h) { return min(kStep, t_hi - (t_lo + h * kStep)); };
     const int blk0 = pt[ulo];  // steps 0 and 1 lie in the piece's first block
 
-    // Q^T fragments for this wave's 32 heads, resident for the whole piece
-    const __bf16* qrow = static_cast<const __bf16*>(a.q) +
-                         ((size_t(b) * a.n_q + j) * kH + wave * 32 + hl) * kD;
+    // Q^T fragments for this wave's 32 heads, resident for the whole piece.
+    // The 32 heads' rows of a wave are one contiguous 36 KB block -- a step
+    // tile -- so Q is staged through the step buffers with the cache loads'
+    // own direct loads and layout (wave t's block into buffer t), and each
+    // wave reads its fragments exactly like K fragments: whole-row loads
+    // instead of 16-byte pieces of 32 rows per instruction.
+    {
+      const unsigned char* qblk = static_cast<const unsigned char*>(a.q) +
+                                  (size_t(b) * a.n_q + j) * kH * kRowBytes;
+#pragma unroll
+      for (int t = 0; t < kNT / kWave; ++t) load_step(bbuf(t), qblk + t * kStepBytes, kStep, wave, loff);
+    }
+    wait_vm<0>();
+    step_barrier();
     bf16x8 qf[kQK];
+    {
+      const uint32_t qb = lds_addr(bbuf(wave)) + koff0;
 #pragma unroll
-    for (int s = 0; s < kQK; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * g);
-    // step 0 travels with Q; waiting for Q here (the compiler waits for every
-    // older load) keeps that wait from draining later steps inside the loop
-    load_step(sm.buf[0], step_at(blk0, 0), valid_in(0), wave, loff);
-#pragma unroll
-    for (int s = 0; s < kQK; ++s) asm volatile("" ::"v"(qf[s]));
+      for (int s = 0; s < kQK; ++s) qf[s] = lds_b128_at((qb ^ uint32_t((s & 3) << 5)) + uint32_t((s >> 2) * 1024));
+    }
+    step_barrier();  // every wave holds its Q: the buffers are free for the cache
+    if constexpr (kF8)
+      load_f8(0, blk0, 0, valid_in(0));
+    else
+      load_step(bbuf(0), step_at(blk0, 0), valid_in(0), wave, loff);
 
     f32x16 O[kDC / 32];
 #pragma unroll
@@ -264,8 +362,8 @@ void decode_mfma_kernel(DecodeArgs a) {
     // first step has no PV yet; the drain after the last step has no QK.
     auto run_step = [&](auto qk_on, auto pv_on, int h) __attribute__((always_inline)) {
       constexpr bool kQKOn = decltype(qk_on)::value, kPVOn = decltype(pv_on)::value;
-      const uint32_t kb = lds_addr(sm.buf[h % kNBuf]) + koff0;
-      const uint32_t vb = lds_addr(sm.buf[h > 0 ? (h + kNBuf - 1) % kNBuf : 0]) + voff0;
+      const uint32_t kb = lds_addr(bbuf(h % NB)) + koff0;
+      const uint32_t vb = lds_addr(bbuf(h > 0 ? (h + NB - 1) % NB : 0)) + voff0;
       auto kfrag = [&](int n) __attribute__((always_inline)) {  // chunk pair n&3 of sub-block column n>>2
         return lds_b128_at((kb ^ uint32_t((n & 3) << 5)) + uint32_t((n >> 2) * 1024));
       };
@@ -365,28 +463,57 @@ void decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    if (nsteps > 1) load_step(sm.buf[1], step_at(blk0, 1), valid_in(1), wave, loff);
     // block of the next step to prefetch, looked up one step early
     int blk_nx = nsteps > 2 ? pt[ulo + 1] : 0;
-    // Step h waits until its own loads are done (at most the loads of step
-    // h+1, issued one iteration earlier, still pending), then a barrier makes
-    // every wave's share visible and frees buffer (h+2)%4 for the next load.
-    auto begin_step = [&](int h) __attribute__((always_inline)) {
-      if (h + 1 < nsteps)
-        wait_vm<kLoadsPerWave>();
+    if constexpr (!kF8) {
+      if (nsteps > 1) load_step(bbuf(1), step_at(blk0, 1), valid_in(1), wave, loff);
+      // Step h waits until its own loads are done (at most the loads of step
+      // h+1, issued one iteration earlier, still pending), then a barrier makes
+      // every wave's share visible and frees buffer (h+2)%4 for the next load.
+      auto begin_step = [&](int h) __attribute__((always_inline)) {
+        if (h + 1 < nsteps)
+          wait_vm<kLoadsPerWave>();
+        else
+          wait_vm<0>();
+        step_barrier();
+        if (h + 2 < nsteps)
+          load_step(bbuf((h + 2) % kNBuf), step_at(blk_nx, h + 2), valid_in(h + 2), wave, loff);
+        if (h + 3 < nsteps) blk_nx = pt[ulo + ((h + 3) >> 1)];
+      };
+      // Step 0 runs the same code with P = 0 against its own (finite, zero-filled
+      // past the length) buffer: a second specialisation without PV costs the
+      // register allocator more than these 32 MFMAs cost the piece.
+      for (int h = 0; h < nsteps; ++h) {
+        begin_step(h);
+        run_step(std::true_type{}, std::true_type{}, h);
+      }
+    } else {
+      // fp8: step h's codes land in staging buffer h%2 and are dequantised
+      // into bf16 step buffer h%3 at the end of iteration h-1, which then
+      // needs one more barrier.  That leaves the load of step h+2 (issued at
+      // the top of iteration h) two iterations to arrive.  A wave issues 4 or
+      // 5 loads per step, so vmcnt(4) means "every earlier step has landed".
+      if (nsteps > 1) load_f8(1, blk0, 1, valid_in(1));
+      if (nsteps > 1)
+        wait_vm<4>();
       else
         wait_vm<0>();
       step_barrier();
-      if (h + 2 < nsteps)
-        load_step(sm.buf[(h + 2) % kNBuf], step_at(blk_nx, h + 2), valid_in(h + 2), wave, loff);
-      if (h + 3 < nsteps) blk_nx = pt[ulo + ((h + 3) >> 1)];
-    };
-    // Step 0 runs the same code with P = 0 against its own (finite, zero-filled
-    // past the length) buffer: a second specialisation without PV costs the
-    // register allocator more than these 32 MFMAs cost the piece.
-    for (int h = 0; h < nsteps; ++h) {
-      begin_step(h);
-      run_step(std::true_type{}, std::true_type{}, h);
+      convert_step_f8(bbuf(0), stage_buf(0), valid_in(0));
+      for (int h = 0; h < nsteps; ++h) {
+        step_barrier();  // step h converted; staging buffer h%2 free again
+        if (h + 2 < nsteps) load_f8(h & 1, blk_nx, h + 2, valid_in(h + 2));
+        if (h + 3 < nsteps) blk_nx = pt[ulo + ((h + 3) >> 1)];
+        run_step(std::true_type{}, std::true_type{}, h);
+        if (h + 1 < nsteps) {
+          if (h + 2 < nsteps)
+            wait_vm<4>();
+          else
+            wait_vm<0>();
+          step_barrier();
+          convert_step_f8(bbuf((h + 1) % kF8NBuf), stage_buf((h + 1) & 1), valid_in(h + 1));
+        }
+      }
     }
     run_step(std::false_type{}, std::true_type{}, nsteps);  // PV of the last step
     o_ready(O);
@@ -402,7 +529,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
     if (lane < 32) a.ws_lse[orow0 + lane] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
-    unsigned char* stage = &sm.buf[0][0] + wave * (32 * kStageRow);
+    unsigned char* stage = sm.lds + wave * (32 * kStageRow);
 #pragma unroll
     for (int cb = 0; cb < kDC / 32; ++cb)
 #pragma unroll
@@ -424,23 +551,30 @@ void decode_mfma_kernel(DecodeArgs a) {
 }  // namespace
 
 bool decode_mfma_supported(const DecodeArgs& a) {
-  return a.H == kH && a.d_latent == kDC && a.D == kD && a.block_size == kBS &&
-         a.act_dtype == MLA_BF16 && a.cache_dtype == MLA_BF16 &&
-         (reinterpret_cast<uintptr_t>(a.cache) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.q) % 16) == 0;
+  const bool cache_ok =
+      a.cache_dtype == MLA_BF16 ||
+      (a.cache_dtype == MLA_FP8_E4M3 && a.scales != nullptr && (reinterpret_cast<uintptr_t>(a.scales) % 16) == 0);
+  return a.H == kH && a.d_latent == kDC && a.D == kD && a.block_size == kBS && a.act_dtype == MLA_BF16 &&
+         cache_ok && (reinterpret_cast<uintptr_t>(a.cache) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.q) % 16) == 0;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+template <bool kF8>
+hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t st) {
   static bool attr_set = false;
   const size_t smem = sizeof(Smem);
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel<kF8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid(unsigned(a.G) * unsigned(a.n_q));
-  hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(kNT), smem, st, a);
+  hipLaunchKernelGGL(decode_mfma_kernel<kF8>, grid, dim3(kNT), smem, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+  return a.cache_dtype == MLA_FP8_E4M3 ? launch_decode_mfma_t<true>(a, st) : launch_decode_mfma_t<false>(a, st);
 }
 
 }  // namespace mla

@@ -13,8 +13,8 @@ import torch
 
 import mla_workloads as W
 from oracle import mla_oracle as O
-from tests.cases import (DT, DecodeCase, append_workspace, compare_sampled, dims_of, max_abs,
-                         rel_l2, to_f64)
+from tests.cases import (DT, DecodeCase, append_workspace, compare_sampled, dims_of, fp8_score_bound,
+                         max_abs, rel_l2, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -289,7 +289,7 @@ def test_out_proj_v3_bf16():
 # --------------------------------------------------------------------------
 # full-size workloads, default launch configuration, sampled sequences
 # --------------------------------------------------------------------------
-FULL = {"v3": [0, 17, 63], "long": [0, 3]}
+FULL = {"v3": [0, 17, 63], "long": [0, 3], "fp8": [0, 77, 127]}
 
 
 @pytest.mark.parametrize("name", sorted(FULL))
@@ -297,7 +297,10 @@ def test_full_size_sampled(name):
     cfg = W.CONFIGS[name]
     case = DecodeCase(cfg)
     u, lse = case.run()
-    compare_sampled(case, u, lse, FULL[name])
+    if cfg.cache_dtype == "fp8":
+        compare_sampled(case, u, lse, FULL[name], rel_bar=5e-2, abs_bar=None)
+    else:
+        compare_sampled(case, u, lse, FULL[name])
     assert torch.isfinite(u.float()).all()
 
 
@@ -333,6 +336,40 @@ def test_decode_mfma_small(idx, G):
     case = DecodeCase(cfg)
     u, lse = case.run(G=G)
     compare_sampled(case, u, lse, list(range(cfg.batch)))
+
+
+# fp8-e4m3 cache: the MFMA kernel dequantises each step into bf16 in LDS
+MFMA_FP8 = [
+    W.scaled(W.CONFIGS["fp8"], batch=3, seq_len=333),
+    W.scaled(W.CONFIGS["fp8"], batch=2, seq_len=64),
+    W.scaled(W.CONFIGS["fp8"], batch=4, seq_len=1),
+    W.scaled(W.CONFIGS["fp8"], batch=3, seq_len=97),
+]
+
+
+@pytest.mark.parametrize("G", [1, 3, 64])
+@pytest.mark.parametrize("idx", range(len(MFMA_FP8)))
+def test_decode_mfma_fp8_small(idx, G):
+    cfg = MFMA_FP8[idx]
+    case = DecodeCase(cfg)
+    u, lse = case.run(G=G)
+    compare_sampled(case, u, lse, list(range(cfg.batch)), rel_bar=5e-2, abs_bar=None)
+    assert torch.isfinite(u.float()).all()
+
+
+def test_decode_mfma_fp8_agrees_with_generic():
+    """Both fp8 paths decode the same codes and scales; they differ only in
+    where the values are rounded (bf16 operands vs fp32 products)."""
+    import mla_latent_kv_decode_amd as M
+    cfg = W.scaled(W.CONFIGS["fp8"], batch=5, seq_len=900)
+    case = DecodeCase(cfg)
+    u1, l1 = case.run(G=16)
+    u2, l2 = case.run(flags=M.FLAG_GENERIC_DECODE, G=16)
+    assert rel_l2(to_f64(u1), to_f64(u2)) <= 5e-3
+    # the generic path's products are exact in fp32: the two differ by at most
+    # the bf16 rounding bound of the MFMA path (plus fp32 noise)
+    tol = np.stack([1e-3 + fp8_score_bound(case, b) for b in range(cfg.batch)])
+    assert np.all(np.abs(l1.cpu().numpy() - l2.cpu().numpy()) <= tol)
 
 
 def test_decode_mfma_agrees_with_generic():
