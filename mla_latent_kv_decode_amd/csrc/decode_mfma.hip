@@ -199,7 +199,8 @@ MLA_DEV void convert_step_f8(unsigned char* dst, const unsigned char* stage, int
   typedef __attribute__((address_space(3))) const float lds_f32;
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const uint32_t sb = lds_addr(stage), db = lds_addr(dst);
-  for (int u = threadIdx.x; u < kStep * (kD / 16); u += kNT) {
+#pragma unroll 1
+  for (int u = tid_fresh(); u < kStep * (kD / 16); u += kNT) {
     const int t = u / (kD / 16), c8 = u % (kD / 16);
     const u32x4 cw = *(lds_u4*)(uintptr_t)(sb + t * kD + c8 * 16);
     const float sc_raw = *(lds_f32*)(uintptr_t)(sb + kF8Codes + (t * 5 + c8 / 8) * 4);
@@ -248,6 +249,15 @@ MLA_DEV void scores_ready(f32x16& s) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop
 MLA_DEV void mfma_pv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// O = 0 straight into the AGPRs (an MFMA on zero operands with a zero
+// accumulator); volatile, so it is not hoisted out of the piece loop as a
+// constant that then has to be kept (or spilled) across it.  The zero
+// operand is written by VALU moves just before: an MFMA reading a VGPR that
+// a VALU instruction wrote needs two wait states in between, which the
+// compiler does not insert for inline asm -- hence the s_nop.
+MLA_DEV void zero_acc(f32x16& acc, const bf16x8& z) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+}
 MLA_DEV void o_ready(f32x16 (&O)[16]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]),
@@ -289,8 +299,16 @@ void decode_mfma_kernel(DecodeArgs a) {
   // (+8 tokens moves one 8-token group down and flips swizzle bit 1).  Step
   // buffers are 128-byte aligned, so the XORs commute with adding the base.
   const int h16 = (lane / 16) & 1, s16 = lane % 16;
-  const uint32_t koff0 = uint32_t(step_off(hl, g));
-  const uint32_t voff0 = uint32_t(step_off(4 * g + s16 / 4, 2 * h16 + (s16 % 4) / 2) + 8 * (s16 % 2));
+  // (recomputed from a fresh lane id at every step: two values fewer to keep
+  // live across the piece, which the fp8 path's dequantisation needs)
+  auto koff0_at = [&]() __attribute__((always_inline)) {
+    const int l = tid_fresh() % kWave;
+    return uint32_t(step_off(l % 32, l / 32));
+  };
+  auto voff0_at = [&]() __attribute__((always_inline)) {
+    const int l = tid_fresh() % kWave, gg = l / 32, hh = (l / 16) & 1, ss = l % 16;
+    return uint32_t(step_off(4 * gg + ss / 4, 2 * hh + (ss % 4) / 2) + 8 * (ss % 2));
+  };
   const int loff = load_lane_off(lane, wave & 1);
 
   plan_for_each_piece<kNT>(a.seq_lens, a.batch, kBS, a.G, part, sm.plan,
@@ -305,9 +323,10 @@ void decode_mfma_kernel(DecodeArgs a) {
     const int nsteps = max(0, (t_hi - t_lo + kStep - 1) / kStep);
     const size_t orow0 = (size_t(slot) * a.n_q + j) * kH + wave * 32;
     if (nsteps == 0) {  // nothing visible to this query in the piece
+      const int elane = tid_fresh() % kWave;
       uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.ws_o) + orow0 * kDC);
-      for (int e = lane; e < 32 * kDC / 8; e += kWave) dst[e] = uint4{0u, 0u, 0u, 0u};
-      if (lane < 32) a.ws_lse[orow0 + lane] = -INFINITY;
+      for (int e = elane; e < 32 * kDC / 8; e += kWave) dst[e] = uint4{0u, 0u, 0u, 0u};
+      if (elane < 32) a.ws_lse[orow0 + elane] = -INFINITY;
       return;
     }
     // page table through the constant address space: scalar loads
@@ -340,7 +359,9 @@ void decode_mfma_kernel(DecodeArgs a) {
     step_barrier();
     bf16x8 qf[kQK];
     {
-      const uint32_t qb = lds_addr(bbuf(wave)) + koff0;
+      // (addresses from a fresh lane id: not kept live across the step loop)
+      const int ql = tid_fresh() % kWave;
+      const uint32_t qb = lds_addr(bbuf(wave)) + uint32_t(step_off(ql % 32, ql / 32));
 #pragma unroll
       for (int s = 0; s < kQK; ++s) qf[s] = lds_b128_at((qb ^ uint32_t((s & 3) << 5)) + uint32_t((s >> 2) * 1024));
     }
@@ -351,8 +372,11 @@ void decode_mfma_kernel(DecodeArgs a) {
       load_step(bbuf(0), step_at(blk0, 0), valid_in(0), wave, loff);
 
     f32x16 O[kDC / 32];
+    {
+      const bf16x8 z = {};
 #pragma unroll
-    for (int cb = 0; cb < kDC / 32; ++cb) O[cb] = f32x16{};
+      for (int cb = 0; cb < kDC / 32; ++cb) zero_acc(O[cb], z);
+    }
     float m_ref = -INFINITY, l_run = 0.f;
     bf16x8 p_prev[2] = {}, p_cur[2];  // P of the step before the first: zero
 
@@ -362,8 +386,8 @@ void decode_mfma_kernel(DecodeArgs a) {
     // first step has no PV yet; the drain after the last step has no QK.
     auto run_step = [&](auto qk_on, auto pv_on, int h) __attribute__((always_inline)) {
       constexpr bool kQKOn = decltype(qk_on)::value, kPVOn = decltype(pv_on)::value;
-      const uint32_t kb = lds_addr(bbuf(h % NB)) + koff0;
-      const uint32_t vb = lds_addr(bbuf(h > 0 ? (h + NB - 1) % NB : 0)) + voff0;
+      const uint32_t kb = lds_addr(bbuf(h % NB)) + koff0_at();
+      const uint32_t vb = lds_addr(bbuf(h > 0 ? (h + NB - 1) % NB : 0)) + voff0_at();
       auto kfrag = [&](int n) __attribute__((always_inline)) {  // chunk pair n&3 of sub-block column n>>2
         return lds_b128_at((kb ^ uint32_t((n & 3) << 5)) + uint32_t((n >> 2) * 1024));
       };
@@ -406,7 +430,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         if constexpr (kQKOn) {
           if (k == 0) scores_ready(S);
           if (k == 1 && nv < kStep) {  // past-length tokens of a partial step: -inf
-            const int lim = nv - 4 * g;
+            const int lim = nv - 4 * ((tid_fresh() % kWave) / 32);
 #pragma unroll
             for (int r = 0; r < 16; ++r) S[r] = (8 * (r / 4) + (r % 4) >= lim) ? -INFINITY : S[r];
           }
@@ -526,9 +550,11 @@ void decode_mfma_kernel(DecodeArgs a) {
     // row; the stores are non-temporal.  Scattered or ordinary stores issued
     // right after a piece has streamed through L2 run at a fraction of the
     // write bandwidth, and nothing rereads the partials soon.
+    // lane-derived values are recomputed here rather than kept across the loop
+    const int elane = tid_fresh() % kWave, eg = elane / 32, ehl = elane % 32;
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
-    if (lane < 32) a.ws_lse[orow0 + lane] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+    if (elane < 32) a.ws_lse[orow0 + elane] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
     unsigned char* stage = sm.lds + wave * (32 * kStageRow);
 #pragma unroll
     for (int cb = 0; cb < kDC / 32; ++cb)
@@ -536,13 +562,13 @@ void decode_mfma_kernel(DecodeArgs a) {
       for (int rg = 0; rg < 4; ++rg) {
         const uint32_t lo = pack_bf16x2(O[cb][4 * rg + 0] * inv, O[cb][4 * rg + 1] * inv);
         const uint32_t hi = pack_bf16x2(O[cb][4 * rg + 2] * inv, O[cb][4 * rg + 3] * inv);
-        *reinterpret_cast<uint2*>(stage + hl * kStageRow + (32 * cb + 8 * rg + 4 * g) * 2) = uint2{lo, hi};
+        *reinterpret_cast<uint2*>(stage + ehl * kStageRow + (32 * cb + 8 * rg + 4 * eg) * 2) = uint2{lo, hi};
       }
     // the wave reads back only what it wrote itself: LDS order within a wave suffices
-    u32x4* orow = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws_o) + orow0 * kDC) + lane;
+    u32x4* orow = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws_o) + orow0 * kDC) + elane;
 #pragma unroll 8
     for (int r = 0; r < 32; ++r)
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + r * kStageRow + lane * 16),
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + r * kStageRow + elane * 16),
                                   orow + r * (kDC / 8));
     step_barrier();  // every wave is done with the stage before a next piece loads into it
   });

@@ -106,11 +106,30 @@ MLA_DEV float block_sum(float v, float* red) {
   return r;
 }
 
+// Values every lane holds identically, moved to scalar registers: the
+// compiler cannot prove that a value read back from LDS or computed with
+// vector (e.g. double) arithmetic is wave-uniform, and would otherwise keep
+// it in a vector register for as long as it lives.
+MLA_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// threadIdx.x behind an empty asm: what is derived from it is recomputed
+// where it is used instead of being hoisted out of loops and kept live (or
+// spilled) across long loop bodies that need every register.
+MLA_DEV int tid_fresh() {
+  int t = int(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+MLA_DEV int64_t uniform64(int64_t v) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(v) >> 32))));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
 // Exclusive scan of one int per thread across the workgroup; returns the
-// thread's exclusive prefix and writes the total to *total.
+// thread's exclusive prefix and writes the total (wave-uniform) to *total.
 template <int NT>
 MLA_DEV int block_excl_scan(int v, int* red, int* total) {
-  const int l = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int t = tid_fresh(), l = t % kWave, w = t / kWave;
   int incl = v;
   for (int o = 1; o < kWave; o <<= 1) {
     int t = __shfl_up(incl, o, 64);
@@ -124,7 +143,7 @@ MLA_DEV int block_excl_scan(int v, int* red, int* total) {
     if (i < w) base += red[i];
     tot += red[i];
   }
-  *total = tot;
+  *total = uniform(tot);
   return base + incl - v;
 }
 
@@ -132,7 +151,7 @@ MLA_DEV int block_excl_scan(int v, int* red, int* total) {
 // red holds 2 * NT / 64 ints.
 template <int NT>
 MLA_DEV int2 block_excl_scan2(int va, int vb, int* red, int* tota, int* totb) {
-  const int l = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int t = tid_fresh(), l = t % kWave, w = t / kWave;
   int ia = va, ib = vb;
   for (int o = 1; o < kWave; o <<= 1) {
     const int ta = __shfl_up(ia, o, 64), tb = __shfl_up(ib, o, 64);
@@ -148,8 +167,8 @@ MLA_DEV int2 block_excl_scan2(int va, int vb, int* red, int* tota, int* totb) {
     sa += ra;
     sb += rb;
   }
-  *tota = sa;
-  *totb = sb;
+  *tota = uniform(sa);
+  *totb = uniform(sb);
   return int2{ba + ia - va, bb + ib - vb};
 }
 
@@ -253,7 +272,7 @@ MLA_DEV void plan_for_each_piece(const int32_t* seq_lens, int B, int bs, int G, 
   G = min(G, T);
   if (g >= G) return;
   const PartGrid pg(T, G);
-  const int64_t lo = pg.lo(g), hi = pg.lo(g + 1);
+  const int64_t lo = uniform64(pg.lo(g)), hi = uniform64(pg.lo(g + 1));
   if (lo >= hi) return;
   int totP;
   int cnt = plan_chunk<NT>(0, len0, S0, bs, pg, g, lo, hi, 0, sc, &totP);
