@@ -298,16 +298,20 @@ void decode_mfma_kernel(DecodeArgs a) {
   //  4*cbo + 2*h16 + (s16%4)/2, half s16%2):   (voff0 ^ (cbo << 6) ^ (sec << 5)) + sec * 9216
   // (+8 tokens moves one 8-token group down and flips swizzle bit 1).  Step
   // buffers are 128-byte aligned, so the XORs commute with adding the base.
-  const int h16 = (lane / 16) & 1, s16 = lane % 16;
-  // (recomputed from a fresh lane id at every step: two values fewer to keep
-  // live across the piece, which the fp8 path's dequantisation needs)
+  auto koff0_of = [](int l) __attribute__((always_inline)) { return uint32_t(step_off(l & 31, l >> 5)); };
+  auto voff0_of = [](int l) __attribute__((always_inline)) {
+    const int gg = l >> 5, hh = (l >> 4) & 1, ss = l & 15;
+    return uint32_t(step_off(4 * gg + (ss >> 2), 2 * hh + ((ss & 3) >> 1)) + 8 * (ss & 1));
+  };
+  // bf16: kept in two registers for the whole kernel.  fp8: recomputed from
+  // a fresh lane id at every step -- two registers fewer across the loop,
+  // which the dequantisation needs to stay spill-free.
+  const uint32_t koff0 = koff0_of(lane), voff0 = voff0_of(lane);
   auto koff0_at = [&]() __attribute__((always_inline)) {
-    const int l = tid_fresh() % kWave;
-    return uint32_t(step_off(l % 32, l / 32));
+    if constexpr (kF8) return koff0_of(tid_fresh() & (kWave - 1)); else return koff0;
   };
   auto voff0_at = [&]() __attribute__((always_inline)) {
-    const int l = tid_fresh() % kWave, gg = l / 32, hh = (l / 16) & 1, ss = l % 16;
-    return uint32_t(step_off(4 * gg + ss / 4, 2 * hh + (ss % 4) / 2) + 8 * (ss % 2));
+    if constexpr (kF8) return voff0_of(tid_fresh() & (kWave - 1)); else return voff0;
   };
   const int loff = load_lane_off(lane, wave & 1);
 
@@ -378,7 +382,8 @@ void decode_mfma_kernel(DecodeArgs a) {
       for (int cb = 0; cb < kDC / 32; ++cb) zero_acc(O[cb], z);
     }
     float m_ref = -INFINITY, l_run = 0.f;
-    bf16x8 p_prev[2] = {}, p_cur[2];  // P of the step before the first: zero
+    bf16x8 p_prev[2] = {};  // P of the step before the first: zero
+    uint32_t p_cur[2][4];   // P of the current step, bf16 pairs
 
     // One pipeline step.  QK: S^T = K . Q^T for step h (36 MFMAs).  PV: O^T +=
     // V^T . P^T for step h-1 (32 MFMAs), with the softmax of step h spread
@@ -391,8 +396,12 @@ void decode_mfma_kernel(DecodeArgs a) {
       auto kfrag = [&](int n) __attribute__((always_inline)) {  // chunk pair n&3 of sub-block column n>>2
         return lds_b128_at((kb ^ uint32_t((n & 3) << 5)) + uint32_t((n >> 2) * 1024));
       };
+      // output MFMA n updates O block n/2 with token half n%2: the two updates
+      // of a block run back to back, so the second takes the first's result
+      // from the matrix core instead of re-reading the AGPRs (less register
+      // file traffic, which shows up as a higher sustained clock)
       auto vfrag = [&](int n) __attribute__((always_inline)) {
-        const int i = n >> 4, cb = n & 15;
+        const int i = n & 1, cb = n >> 1;
         const uint32_t base = uint32_t((2 * i) * 9216 + (cb >> 1) * 1024);  // token rows 16i..16i+15
         const uint32_t v = vb ^ uint32_t((cb & 1) << 6);
         return lds_tr_pair_at(v + base, (v ^ 32u) + base + 9216u);
@@ -449,13 +458,15 @@ void decode_mfma_kernel(DecodeArgs a) {
             m_ref = m_new;
           }
           if (k >= 4 && k < 12) {
-            const int i = (k - 4) >> 2, e0 = 2 * ((k - 4) & 3);
-#pragma unroll
-            for (int e = e0; e < e0 + 2; ++e) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_log2, -m_ref));
-              lsum += p;
-              p_cur[i][e] = (__bf16)p;
-            }
+            const int i = (k - 4) >> 2, e = 2 * ((k - 4) & 3);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_log2, -m_ref));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e + 1], c_log2, -m_ref));
+            lsum += p0;
+            lsum += p1;
+            p_cur[i][e / 2] = pack_bf16x2(p0, p1);
+            // pin the work here, between the output MFMAs: left alone, the
+            // compiler sinks it to the end of the step where nothing hides it
+            asm volatile("" : "+v"(p_cur[i][e / 2]), "+v"(lsum));
           }
         }
       };
@@ -463,7 +474,7 @@ void decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kPVOn) {
 #pragma unroll
         for (int n = 0; n < kPV; ++n) {
-          mfma_pv(O[n & 15], vr[n % kRV], p_prev[n >> 4]);
+          mfma_pv(O[n >> 1], vr[n % kRV], p_prev[n & 1]);
           if (n + kRV < kPV) vr[n % kRV] = vfrag(n + kRV);
           softmax_part(n);
           __builtin_amdgcn_sched_barrier(0);
@@ -482,8 +493,9 @@ void decode_mfma_kernel(DecodeArgs a) {
           }
         }
         l_run = l_run * corr + lsum;
-        p_prev[0] = p_cur[0];
-        p_prev[1] = p_cur[1];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          p_prev[i] = __builtin_bit_cast(bf16x8, u32x4{p_cur[i][0], p_cur[i][1], p_cur[i][2], p_cur[i][3]});
       }
     };
 
