@@ -7,9 +7,12 @@
 //
 // One workgroup per (head, 32 rows); d_latent = 512, d_v <= 128 (multiple of
 // 32), bf16 partials and weights, fp32 accumulation.
-//  * The head's W^UV_i (d_v rows of 1 KB) is copied into LDS first, one direct
-//    1 KB load per row with the 16-byte chunks XOR-swizzled by row; it streams
-//    in while the workgroup merges the partials.
+//  * The head's W^UV_i (d_v rows of 1 KB) is copied into LDS by direct 1 KB
+//    loads (16-byte chunks XOR-swizzled by row), issued first: it streams in
+//    while the workgroup plans and merges.  The sequence lengths the plan
+//    needs are staged in LDS the same way (one wave, waited for before its
+//    share of W is issued), and the plan's barriers are LDS-only, so nothing
+//    waits for W until the MFMAs.
 //  * Each wave merges 8 rows: every lane owns 8 channels; the lse values and
 //    partial rows of a chunk of 4 pieces are loaded for all 8 rows before any
 //    is used.  The merged u row is rounded to bf16 (as mla_decode_combine
@@ -40,10 +43,15 @@ struct Smem {
   alignas(128) unsigned char w[kMaxDV * kRowBytes];  // W^UV_i
   alignas(128) unsigned char u[kRows * kRowBytes];   // merged rows (bf16)
 };
-// the plan scratch and slot tables live in the u tile until it is written
+// the plan scratch, slot tables and staged lengths live in the u tile until
+// it is written
 constexpr int kMaxSeq = kRows + 1;
-static_assert(sizeof(PlanScratch<kNT>) + 2 * kMaxSeq * sizeof(int) <= kRows * kRowBytes,
-              "plan scratch must fit the u tile");
+constexpr int kLensOff = 5632;        // 256-byte aligned, past scratch and tables
+constexpr int kMaxLensLds = 4096;     // sequences whose lengths are staged in LDS
+static_assert(sizeof(PlanScratch<kNT>) + 2 * kMaxSeq * sizeof(int) <= kLensOff &&
+                  kLensOff + kMaxLensLds * 4 <= kRows * kRowBytes,
+              "plan scratch, tables and lengths must fit the u tile");
+typedef __attribute__((address_space(3))) const int32_t lds_i32;
 
 MLA_DEV uint32_t lds_addr(const unsigned char* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_u8*)p));
@@ -66,9 +74,7 @@ void combine_out_proj_kernel(CombineProjArgs a) {
   const int h = logical / ngroups, r0 = (logical % ngroups) * kRows;
   const int nrows = min(kRows, R - r0);
 
-  // W^UV_i -> LDS: dv/4 rows per wave, one 1 KB direct load each.  Issued
-  // after the first chunk's partial loads: vector-memory operations complete
-  // in order, so waiting for those loads then never waits for W.
+  // W^UV_i -> LDS: dv/4 rows per wave, one 1 KB direct load each.
   auto load_w = [&]() {
     const unsigned char* wsrc = static_cast<const unsigned char*>(a.w_uv) + size_t(h) * dv * kRowBytes;
     const __amdgpu_buffer_rsrc_t rs =
@@ -85,13 +91,32 @@ void combine_out_proj_kernel(CombineProjArgs a) {
     }
   };
 
+  // ---- 0. lengths (wave 0) and W^UV_i (all waves) into LDS ----
+  const bool lens_in_lds = a.batch <= kMaxLensLds && (reinterpret_cast<uintptr_t>(a.seq_lens) % 16) == 0;
+  if (lens_in_lds && wave == 0) {
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.seq_lens, (short)0, a.batch * 4, 0x00020000);
+    for (int k = 0; k * 1024 < a.batch * 4; ++k)
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                   :
+                   : "v"(lane * 16), "s"(rl), "s"(k * 1024), "{m0}"(lds_addr(sm.u + kLensOff + k * 1024))
+                   : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only the lengths are in flight
+  }
+  load_w();
+  lds_barrier();
+
   // ---- 1. first slot and piece count of this group's sequences ----
   PlanScratch<kNT>& ps = *reinterpret_cast<PlanScratch<kNT>*>(sm.u);
   int* t_slot0 = reinterpret_cast<int*>(sm.u + sizeof(PlanScratch<kNT>));
   int* t_np = t_slot0 + kMaxSeq;
   const int b_lo = r0 / a.n_q;
   const int nb = (r0 + nrows - 1) / a.n_q - b_lo + 1;
-  plan_slots<kNT>(a.seq_lens, a.batch, a.block_size, a.G, b_lo, nb, ps, t_slot0, t_np);
+  if (lens_in_lds)
+    plan_slots<kNT>((lds_i32*)(uintptr_t)lds_addr(sm.u + kLensOff), a.batch, a.block_size, a.G, b_lo, nb, ps,
+                    t_slot0, t_np);
+  else
+    plan_slots<kNT>(a.seq_lens, a.batch, a.block_size, a.G, b_lo, nb, ps, t_slot0, t_np);
   int slot0[kRowsPerWave], np[kRowsPerWave], maxnp = 0;
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
@@ -105,7 +130,7 @@ void combine_out_proj_kernel(CombineProjArgs a) {
       maxnp = max(maxnp, np[i]);
     }
   }
-  __syncthreads();  // the tables are read; the u tile may be overwritten
+  lds_barrier();  // the tables are read; the u tile may be overwritten
 
   // ---- 2. merge the pieces of this wave's 8 rows (lane = 8 channels) ----
   float M[kRowsPerWave], wsum[kRowsPerWave], acc[kRowsPerWave][8];
@@ -128,25 +153,39 @@ void combine_out_proj_kernel(CombineProjArgs a) {
     lrow[i] = a.ws_lse + r;
     orow_ws[i] = static_cast<const uint16_t*>(a.ws_o) + r * kDC + 8 * lane;
   }
-  if (maxnp == 0) load_w();  // no pieces at all (then u is zero)
+  static_assert(kRowsPerWave * kPC <= kWave, "one lse per lane");
+  // lane l < 32 fetches the lse of (row l / kPC, piece s0 + l % kPC)
+  const int li = min(lane / kPC, kRowsPerWave - 1), lsp = lane % kPC;
+  int l_np = 0;
+  const float* l_lrow = lrow[0];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i)
+    if (li == i) {
+      l_np = np[i];
+      l_lrow = lrow[i];
+    }
   for (int s0 = 0; s0 < maxnp; s0 += kPC) {
     float ls[kRowsPerWave][kPC];
     uint4 x[kRowsPerWave][kPC];
+    // Loads are unconditional (a branch around each would make the wave wait
+    // for every load before issuing the next): a piece past the row's count
+    // reads the row's last piece (a row with none reads slot 0) and is masked
+    // below by lse = -inf.
+    const int lp = max(0, min(s0 + lsp, l_np - 1));
+    const float lse_l = l_lrow[l_np > 0 ? size_t(lp) * pstride : 0];
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i)
 #pragma unroll
       for (int s = 0; s < kPC; ++s) {
-        // Loads are unconditional (a branch around each would make the wave
-        // wait for every load before issuing the next): a piece past the
-        // row's count reads the row's last piece (a row with none reads
-        // slot 0) and is masked below by lse = -inf.
         const int p = max(0, min(s0 + s, np[i] - 1));
         const size_t off = size_t(p) * pstride;
-        ls[i][s] = lrow[i][np[i] > 0 ? off : 0];
         x[i][s] = *reinterpret_cast<const uint4*>(orow_ws[i] + (np[i] > 0 ? off * kDC : 0));
       }
-    if (s0 == 0) load_w();
     __builtin_amdgcn_sched_barrier(0);  // every load of the chunk is issued before the first use
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+      for (int s = 0; s < kPC; ++s) ls[i][s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse_l), i * kPC + s));
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i)
 #pragma unroll

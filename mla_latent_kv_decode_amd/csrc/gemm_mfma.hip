@@ -123,6 +123,80 @@ __global__ __launch_bounds__(kNT) void append_partial_kernel(AppendArgs a, float
 }
 
 // --------------------------------------------------------------------------
+// append, step 1 (tiled form, used when d_latent and d_rope are multiples of
+// 64 and d_model of 256 -- DeepSeek-V3's 512 / 64 / 7168): one workgroup per
+// (64 columns, 256-wide k slice, 64 tokens).  Both operand tiles (64 rows x
+// 512 bytes) are copied into LDS with direct 1 KB loads -- two rows per
+// instruction, 16-byte chunks XOR-swizzled by row -- so every request is a
+// whole contiguous KB.  Wave w then computes the 32 x 32 block (token half
+// w & 1, column half w >> 1) over the whole slice: 16 MFMAs, no cross-wave
+// reduction, and stores its fp32 partial straight from the accumulator.
+// --------------------------------------------------------------------------
+constexpr int kTT = 64, kTC = 64, kTK = 256;   // tokens x columns x k slice
+constexpr int kTRow = kTK * 2;                 // 512-byte tile rows
+struct AppTileSmem {
+  alignas(128) unsigned char h[kTT * kTRow];
+  alignas(128) unsigned char w[kTC * kTRow];
+};
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_c;
+MLA_DEV uint32_t lds_addr_u8(const unsigned char* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) unsigned char*)p));
+}
+
+// rows [0, nrows) of a 64-row tile, row r at src + r * row_stride bytes,
+// kTRow bytes each, into dst; rows >= nrows read zeros (descriptor range)
+MLA_DEV void tile_to_lds(unsigned char* dst, const unsigned char* src, int nrows, int row_stride, int wave,
+                         int lane) {
+  const uint32_t range = uint32_t((nrows - 1) * row_stride + kTRow);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, range, 0x00020000);
+  for (int i = wave; i < kTT / 2; i += kNT / kWave) {
+    const int row = 2 * i + (lane >> 5);
+    // lane fills LDS chunk slot lane & 31 of its row with source chunk (lane & 31) ^ (row & 31)
+    const uint32_t voff = uint32_t(row * row_stride + (((lane & 31) ^ (row & 31)) << 4));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "{m0}"(lds_addr_u8(dst + i * 1024))
+                 : "memory");
+  }
+}
+
+__global__ __launch_bounds__(kNT) void append_partial_tiled_kernel(AppendArgs a, float* ws) {
+  extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
+  AppTileSmem& sm = *reinterpret_cast<AppTileSmem*>(smem_raw);
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int c0 = blockIdx.x * kTC, kc = blockIdx.y, t0 = blockIdx.z * kTT;
+  const int T = a.n_tokens, D = a.D, dm = a.d_model, dc = a.d_latent;
+  const int64_t k0 = int64_t(kc) * kTK;
+  const unsigned char* hsrc = static_cast<const unsigned char*>(a.h) + (int64_t(t0) * dm + k0) * 2;
+  const unsigned char* wsrc =
+      c0 < dc ? static_cast<const unsigned char*>(a.w_dkv) + (int64_t(c0) * dm + k0) * 2
+              : static_cast<const unsigned char*>(a.w_kr) + (int64_t(c0 - dc) * dm + k0) * 2;
+  tile_to_lds(sm.h, hsrc, min(kTT, T - t0), dm * 2, wave, lane);
+  tile_to_lds(sm.w, wsrc, kTC, dm * 2, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  const int m = lane % 32, g = lane / 32, th = wave & 1, ch = wave >> 1;
+  const uint32_t ha = lds_addr_u8(sm.h) + uint32_t((32 * th + m) * kTRow);
+  const uint32_t wa = lds_addr_u8(sm.w) + uint32_t((32 * ch + m) * kTRow);
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < kTK / 16; ++s) {
+    const uint32_t slot = uint32_t(((2 * s + g) ^ m) << 4);  // row & 31 == m
+    const bf16x8 av = *(lds_bf16x8_c*)(uintptr_t)(ha + slot);
+    const bf16x8 bv = *(lds_bf16x8_c*)(uintptr_t)(wa + slot);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  }
+  // lane (g, m) holds tokens 8*(r/4) + 4*g + r%4 (of this half) of column m
+  const int col = c0 + 32 * ch + m;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = t0 + 32 * th + 8 * (r / 4) + 4 * g + (r % 4);
+    if (t < T) ws[(int64_t(kc) * T + t) * D + col] = acc[r];
+  }
+}
+
+// --------------------------------------------------------------------------
 // append, step 2: one 128-thread workgroup per (token, 128-channel tile): sum
 // the k-slice partials of its columns, rotate k^R (rotate-half pairs
 // (j, j + d_R/2), angle pos * base^(-j/(d_R/2)) in fp64, cos/sin rounded to
@@ -139,21 +213,41 @@ __global__ __launch_bounds__(kFinNT) void append_finalize_kernel(AppendArgs a, c
   const int D = a.D, dc = a.d_latent, T = a.n_tokens;
   const int c = tile * kFinNT + tid;
   float v = 0.f;
-  if (c < D) {
-    const float* p = ws + int64_t(t) * D + c;
+  int pos = 0;
+  int64_t row = 0;
+  {
+    // All partials of a chunk are loaded before any is added (unconditional
+    // loads of clamped indices, masked after): one memory round trip per 32
+    // slices; the sum order is fixed (deterministic).  The token's position
+    // and cache row (two dependent scalar lookups) are fetched while the
+    // first chunk is in flight.
+    const float* p = ws + int64_t(t) * D + min(c, D - 1);
     const int64_t stride = int64_t(T) * D;
-    float s0 = 0.f, s1 = 0.f;  // two chains, fixed order: deterministic
-    int kc = 0;
-    for (; kc + 1 < nk; kc += 2) {
-      s0 += p[int64_t(kc) * stride];
-      s1 += p[int64_t(kc + 1) * stride];
+    constexpr int kChunk = 32;
+    for (int kc0 = 0; kc0 < nk; kc0 += kChunk) {
+      float x[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) x[i] = p[int64_t(min(kc0 + i, nk - 1)) * stride];
+      __builtin_amdgcn_sched_barrier(0);
+      if (kc0 == 0) {
+        pos = a.positions[t];
+        const int blk = a.page_table[int64_t(a.seq_ids[t]) * a.max_blocks + pos / a.block_size];
+        row = int64_t(blk) * a.block_size + pos % a.block_size;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        if (kc0 + i >= nk) x[i] = 0.f;
+#pragma unroll
+      for (int w = kChunk / 2; w > 0; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) x[i] += x[i + w];
+      v += x[0];
     }
-    if (kc < nk) s0 += p[int64_t(kc) * stride];
-    v = s0 + s1;
+    if (c >= D) v = 0.f;
   }
   y[tid] = v;
   __syncthreads();
-  const int pos = a.positions[t];
   const int half = a.d_rope / 2;
   const int jr = c - dc;
   if (jr >= 0 && jr < half) {  // this thread owns the pair (jr, jr + half)
@@ -165,8 +259,6 @@ __global__ __launch_bounds__(kFinNT) void append_finalize_kernel(AppendArgs a, c
   }
   __syncthreads();
   v = y[tid];
-  const int blk = a.page_table[int64_t(a.seq_ids[t]) * a.max_blocks + pos / a.block_size];
-  const int64_t row = int64_t(blk) * a.block_size + pos % a.block_size;
   if constexpr (CDT == MLA_BF16) {
     if (c < D) static_cast<uint16_t*>(a.cache)[row * D + c] = f32_to_bf16(v);
   } else if constexpr (CDT == MLA_FP32) {
@@ -207,6 +299,12 @@ static void append_split(const AppendArgs& a, int* nk, int* kslice) {
   *nk = (a.d_model + ks - 1) / ks;
 }
 
+// The tiled partial kernel needs column tiles that do not straddle W^DKV /
+// W^KR and k slices that divide the model dimension.
+static bool append_tiled(const AppendArgs& a) {
+  return a.d_latent % kTC == 0 && a.d_rope % kTC == 0 && a.d_model % kTK == 0;
+}
+
 bool append_mfma_supported(const AppendArgs& a) {
   return a.act_dtype == MLA_BF16 && a.d_model % 16 == 0 && a.D <= 1024 && a.D % 4 == 0 &&
          (reinterpret_cast<uintptr_t>(a.h) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.w_dkv) % 16) == 0 &&
@@ -216,14 +314,29 @@ bool append_mfma_supported(const AppendArgs& a) {
 size_t append_mfma_workspace(const AppendArgs& a) {
   int nk, ks;
   append_split(a, &nk, &ks);
+  if (append_tiled(a)) nk = a.d_model / kTK;
   return size_t(nk) * size_t(a.n_tokens) * size_t(a.D) * sizeof(float);
 }
 
 hipError_t launch_append_mfma(const AppendArgs& a, void* ws, hipStream_t st) {
   int nk, ks;
   append_split(a, &nk, &ks);
-  dim3 g1(unsigned((a.D + kAppCol - 1) / kAppCol), unsigned(nk), unsigned((a.n_tokens + kAppTok - 1) / kAppTok));
-  hipLaunchKernelGGL(append_partial_kernel, g1, dim3(kNT), 0, st, a, static_cast<float*>(ws), ks);
+  if (append_tiled(a)) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(append_partial_tiled_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(AppTileSmem)));
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    nk = a.d_model / kTK;
+    dim3 g1(unsigned(a.D / kTC), unsigned(nk), unsigned((a.n_tokens + kTT - 1) / kTT));
+    hipLaunchKernelGGL(append_partial_tiled_kernel, g1, dim3(kNT), sizeof(AppTileSmem), st, a,
+                       static_cast<float*>(ws));
+  } else {
+    dim3 g1(unsigned((a.D + kAppCol - 1) / kAppCol), unsigned(nk), unsigned((a.n_tokens + kAppTok - 1) / kAppTok));
+    hipLaunchKernelGGL(append_partial_kernel, g1, dim3(kNT), 0, st, a, static_cast<float*>(ws), ks);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(unsigned(a.n_tokens), unsigned((a.D + kFinNT - 1) / kFinNT));

@@ -106,6 +106,13 @@ MLA_DEV float block_sum(float v, float* red) {
   return r;
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then s_barrier.  Unlike __syncthreads() it carries no fence, so
+// the compiler does not wait for outstanding global loads first -- loads
+// issued earlier (e.g. weights streamed into LDS by direct loads) stay in
+// flight across it.  Every barrier of the partition plan is of this kind.
+MLA_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Values every lane holds identically, moved to scalar registers: the
 // compiler cannot prove that a value read back from LDS or computed with
 // vector (e.g. double) arithmetic is wave-uniform, and would otherwise keep
@@ -135,9 +142,9 @@ MLA_DEV int block_excl_scan(int v, int* red, int* total) {
     int t = __shfl_up(incl, o, 64);
     if (l >= o) incl += t;
   }
-  __syncthreads();
+  lds_barrier();
   if (l == kWave - 1) red[w] = incl;
-  __syncthreads();
+  lds_barrier();
   int base = 0, tot = 0;
   for (int i = 0; i < NT / kWave; ++i) {
     if (i < w) base += red[i];
@@ -157,9 +164,9 @@ MLA_DEV int2 block_excl_scan2(int va, int vb, int* red, int* tota, int* totb) {
     const int ta = __shfl_up(ia, o, 64), tb = __shfl_up(ib, o, 64);
     if (l >= o) { ia += ta; ib += tb; }
   }
-  __syncthreads();
+  lds_barrier();
   if (l == kWave - 1) { red[w] = ia; red[NT / kWave + w] = ib; }
-  __syncthreads();
+  lds_barrier();
   int ba = 0, bb = 0, sa = 0, sb = 0;
   for (int i = 0; i < NT / kWave; ++i) {
     const int ra = red[i], rb = red[NT / kWave + i];
@@ -218,8 +225,9 @@ struct PlanScratch {
 // T = total units.  Also returns the first chunk's per-thread length,
 // exclusive unit prefix and unit total, which the callers reuse (the whole
 // plan when B <= NT).
-template <int NT>
-MLA_DEV int plan_total_units(const int32_t* seq_lens, int B, int bs, PlanScratch<NT>& sc, int* len0,
+// seq_lens may be a global pointer or an LDS copy (LenP = its pointer type).
+template <int NT, class LenP>
+MLA_DEV int plan_total_units(LenP seq_lens, int B, int bs, PlanScratch<NT>& sc, int* len0,
                              int* S0, int* tot0) {
   int T = 0;
   *len0 = *S0 = *tot0 = 0;
@@ -254,17 +262,17 @@ MLA_DEV int plan_chunk(int c, int len, int S, int bs, const PartGrid& pg, int g,
     sc.slot[r.y] = carryP + r.x + (g - first);
     sc.len[r.y] = len;
   }
-  __syncthreads();
+  lds_barrier();
   return cnt;
 }
 
 // Calls f(b, unit_lo, unit_hi, slot, seq_len) (units relative to the
 // sequence start) for every piece of partition g, in sequence order.  All
-// threads call it with identical arguments; f may use __syncthreads.  Only
+// threads call it with identical arguments; f may use barriers.  Only
 // workgroup-uniform values stay live across f (the chunk-0 list is built
 // before the loop), so f gets the whole register file.
-template <int NT, class F>
-MLA_DEV void plan_for_each_piece(const int32_t* seq_lens, int B, int bs, int G, int g,
+template <int NT, class LenP, class F>
+MLA_DEV void plan_for_each_piece(LenP seq_lens, int B, int bs, int G, int g,
                                  PlanScratch<NT>& sc, F&& f) {
   int len0, S0, tot0;
   const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
@@ -285,7 +293,7 @@ MLA_DEV void plan_for_each_piece(const int32_t* seq_lens, int B, int bs, int G, 
     carryS = __builtin_amdgcn_readfirstlane(carryS + totN);
     carryP = __builtin_amdgcn_readfirstlane(carryP + totP);
     c += NT;
-    __syncthreads();  // the next chunk rewrites the piece list
+    lds_barrier();  // the next chunk rewrites the piece list
     const int b = c + int(threadIdx.x);
     const int len = b < B ? seq_lens[b] : 0;
     const int S = carryS + block_excl_scan<NT>(units_of(len, bs), sc.red, &totN);
@@ -295,8 +303,8 @@ MLA_DEV void plan_for_each_piece(const int32_t* seq_lens, int B, int bs, int G, 
 }
 
 // Slot of the first piece of sequence b and its number of pieces.
-template <int NT>
-MLA_DEV void plan_lookup(const int32_t* seq_lens, int B, int bs, int G, int b,
+template <int NT, class LenP>
+MLA_DEV void plan_lookup(LenP seq_lens, int B, int bs, int G, int b,
                          PlanScratch<NT>& sc, int* slot0, int* npieces) {
   int len0, S0, tot0;
   const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
@@ -321,14 +329,14 @@ MLA_DEV void plan_lookup(const int32_t* seq_lens, int B, int bs, int G, int b,
       sc.b[0] = P;
       sc.ulo[0] = pieces;
     }
-    __syncthreads();
+    lds_barrier();
     if (b < c + NT) {
       *slot0 = sc.b[0];
       *npieces = sc.ulo[0];
-      __syncthreads();
+      lds_barrier();
       return;
     }
-    __syncthreads();
+    lds_barrier();
     carryS += totN;
     carryP += totP;
   }
@@ -337,8 +345,8 @@ MLA_DEV void plan_lookup(const int32_t* seq_lens, int B, int bs, int G, int b,
 // First slot and piece count of every sequence in [b_lo, b_lo + nb), written
 // to t_slot0 / t_np (nb entries each, typically LDS).  All threads call it;
 // the tables are complete when it returns.
-template <int NT>
-MLA_DEV void plan_slots(const int32_t* seq_lens, int B, int bs, int G, int b_lo, int nb,
+template <int NT, class LenP>
+MLA_DEV void plan_slots(LenP seq_lens, int B, int bs, int G, int b_lo, int nb,
                         PlanScratch<NT>& sc, int* t_slot0, int* t_np) {
   for (int i = threadIdx.x; i < nb; i += NT) {
     t_slot0[i] = 0;
@@ -369,7 +377,7 @@ MLA_DEV void plan_slots(const int32_t* seq_lens, int B, int bs, int G, int b_lo,
       carryP += totP;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Workspace layout: [o: n_slots][n_q][H][d_latent] in the activation dtype |
