@@ -59,6 +59,23 @@ MLA_DEV uint32_t lds_addr(const unsigned char* p) {
 // byte offset of 16-byte chunk c of row `row` (chunks XOR-swizzled by row)
 MLA_DEV uint32_t chunk_off(int row, int c) { return uint32_t(row * kRowBytes + ((c ^ (row & 15)) << 4)); }
 
+// W^UV_i -> LDS: dv/4 rows per wave, one 1 KB direct load each; lane l fills
+// chunk slot l of its row with source chunk l ^ (row & 15).
+MLA_DEV void load_w_rows(unsigned char* dst, const void* w_uv, int h, int dv, int wave, int lane) {
+  const unsigned char* wsrc = static_cast<const unsigned char*>(w_uv) + size_t(h) * dv * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wsrc, (short)0, dv * kRowBytes, 0x00020000);
+  const int per = dv / (kNT / kWave);
+  for (int i = 0; i < per; ++i) {
+    const int row = wave * per + i;
+    const uint32_t voff = uint32_t((lane ^ (row & 15)) << 4);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(row * kRowBytes), "{m0}"(lds_addr(dst + row * kRowBytes))
+                 : "memory");
+  }
+}
+
 __global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void combine_out_proj_kernel(CombineProjArgs a) {
   extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
@@ -74,22 +91,6 @@ void combine_out_proj_kernel(CombineProjArgs a) {
   const int h = logical / ngroups, r0 = (logical % ngroups) * kRows;
   const int nrows = min(kRows, R - r0);
 
-  // W^UV_i -> LDS: dv/4 rows per wave, one 1 KB direct load each.
-  auto load_w = [&]() {
-    const unsigned char* wsrc = static_cast<const unsigned char*>(a.w_uv) + size_t(h) * dv * kRowBytes;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)wsrc, (short)0, dv * kRowBytes, 0x00020000);
-    const int per = dv / (kNT / kWave);
-    for (int i = 0; i < per; ++i) {
-      const int row = wave * per + i;
-      // lane l fills LDS chunk slot l of the row with source chunk l ^ (row & 15)
-      const uint32_t voff = uint32_t((lane ^ (row & 15)) << 4);
-      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                   :
-                   : "v"(voff), "s"(rs), "s"(row * kRowBytes), "{m0}"(lds_addr(sm.w + row * kRowBytes))
-                   : "memory");
-    }
-  };
 
   // ---- 0. lengths (wave 0) and W^UV_i (all waves) into LDS ----
   const bool lens_in_lds = a.batch <= kMaxLensLds && (reinterpret_cast<uintptr_t>(a.seq_lens) % 16) == 0;
@@ -103,7 +104,7 @@ void combine_out_proj_kernel(CombineProjArgs a) {
                    : "memory");
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only the lengths are in flight
   }
-  load_w();
+  load_w_rows(sm.w, a.w_uv, h, dv, wave, lane);
   lds_barrier();
 
   // ---- 1. first slot and piece count of this group's sequences ----
@@ -268,6 +269,161 @@ void combine_out_proj_kernel(CombineProjArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Few rows (R <= 32, e.g. a handful of long sequences): one workgroup per
+// (head, row).  The four waves split the row's pieces (wave w merges pieces
+// w, w + 4, ...), meet in LDS, and the 256 threads then form the d_v outputs
+// as dot products against W^UV_i in LDS (two threads per output, 256 channels
+// each).  With 64 pieces a row this spreads the merge over H x R workgroups
+// of four busy waves instead of H workgroups with one.
+// ---------------------------------------------------------------------------
+constexpr int kMaxRowModeRows = 32;
+struct RowSmem {
+  alignas(128) unsigned char w[kMaxDV * kRowBytes];  // W^UV_i, rows swizzled as above
+  alignas(16) float acc[kNT / kWave][kDC];           // per-wave unnormalised sums
+  alignas(16) unsigned char u[kRowBytes];            // merged row (bf16)
+  alignas(16) int lens[kMaxRowModeRows * 8];         // staged sequence lengths (B <= R)
+  float mw[kNT / kWave], sw[kNT / kWave];
+  int t_slot0[1], t_np[1];
+  PlanScratch<kNT> plan;
+};
+
+__global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void combine_out_proj_row_kernel(CombineProjArgs a) {
+  extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
+  RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int R = a.batch * a.n_q, H = a.H, dv = a.d_v;
+  const int NB = gridDim.x, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;  // rows of one head share an XCD
+  const int h = logical / R, r = logical % R;
+  const int b = r / a.n_q, j = r % a.n_q;
+
+  // ---- 0. lengths (wave 0) and W^UV_i (all waves) into LDS ----
+  const bool lens_in_lds = (reinterpret_cast<uintptr_t>(a.seq_lens) % 16) == 0;
+  if (lens_in_lds && wave == 0) {
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.seq_lens, (short)0, a.batch * 4, 0x00020000);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(lane * 16), "s"(rl), "{m0}"(lds_addr(reinterpret_cast<unsigned char*>(sm.lens)))
+                 : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  load_w_rows(sm.w, a.w_uv, h, dv, wave, lane);
+  lds_barrier();
+
+  // ---- 1. the row's first slot and piece count ----
+  if (lens_in_lds)
+    plan_slots<kNT>((lds_i32*)(uintptr_t)lds_addr(reinterpret_cast<unsigned char*>(sm.lens)), a.batch,
+                    a.block_size, a.G, b, 1, sm.plan, sm.t_slot0, sm.t_np);
+  else
+    plan_slots<kNT>(a.seq_lens, a.batch, a.block_size, a.G, b, 1, sm.plan, sm.t_slot0, sm.t_np);
+  const int slot0 = __builtin_amdgcn_readfirstlane(sm.t_slot0[0]);
+  const int np = __builtin_amdgcn_readfirstlane(sm.t_np[0]);
+
+  // ---- 2. this wave's pieces: w, w + 4, ... (lane = 8 channels) ----
+  const size_t pstride = size_t(a.n_q) * H;
+  const size_t rbase = (size_t(slot0) * a.n_q + j) * H + h;
+  const float* lrow = a.ws_lse + rbase;
+  const uint16_t* orow = static_cast<const uint16_t*>(a.ws_o) + rbase * kDC + 8 * lane;
+  const int npw = np > wave ? (np - wave + 3) / 4 : 0;
+  float Mw = -INFINITY, swv = 0.f, acc[8] = {};
+  for (int k0 = 0; k0 < npw; k0 += kPC) {
+    // unconditional loads of clamped pieces, masked after (see the row-group kernel)
+    const int pl = wave + 4 * min(k0 + lane % kPC, npw - 1);
+    const float lse_l = lrow[size_t(pl) * pstride];
+    uint4 x[kPC];
+#pragma unroll
+    for (int s = 0; s < kPC; ++s) {
+      const int p = wave + 4 * min(k0 + s, npw - 1);
+      x[s] = *reinterpret_cast<const uint4*>(orow + size_t(p) * pstride * kDC);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float ls[kPC];
+#pragma unroll
+    for (int s = 0; s < kPC; ++s) {
+      ls[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse_l), s));
+      if (k0 + s >= npw) ls[s] = -INFINITY;
+    }
+    float mc = ls[0];
+#pragma unroll
+    for (int s = 1; s < kPC; ++s) mc = fmaxf(mc, ls[s]);
+    const float Mn = fmaxf(Mw, mc);
+    const float sc = Mw == -INFINITY ? 0.f : expf(Mw - Mn);
+    Mw = Mn;
+    swv *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int s = 0; s < kPC; ++s) {
+      const float w = ls[s] == -INFINITY ? 0.f : expf(ls[s] - Mn);
+      swv += w;
+      if (w != 0.f) {
+        const uint32_t v[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += w * __uint_as_float(v[e] << 16);
+          acc[2 * e + 1] += w * __uint_as_float(v[e] & 0xffff0000u);
+        }
+      }
+    }
+  }
+
+  // ---- 3. merge the four waves (thread = 2 channels) ----
+  *reinterpret_cast<float4*>(&sm.acc[wave][8 * lane]) = float4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<float4*>(&sm.acc[wave][8 * lane + 4]) = float4{acc[4], acc[5], acc[6], acc[7]};
+  if (lane == 0) {
+    sm.mw[wave] = Mw;
+    sm.sw[wave] = swv;
+  }
+  lds_barrier();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kNT / kWave; ++w) M = fmaxf(M, sm.mw[w]);
+  float tot = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNT / kWave; ++w) {
+    const float scw = sm.mw[w] == -INFINITY ? 0.f : expf(sm.mw[w] - M);
+    tot += sm.sw[w] * scw;
+    u0 += sm.acc[w][2 * tid] * scw;
+    u1 += sm.acc[w][2 * tid + 1] * scw;
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const uint32_t pk = pack_bf16x2(u0 * inv, u1 * inv);
+  reinterpret_cast<uint32_t*>(sm.u)[tid] = pk;
+  const size_t orow_out = size_t(r) * H + h;  // (b * n_q + j) * H + h
+  if (a.u) reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.u) + orow_out * kDC)[tid] = pk;
+  if (a.lse_out && tid == 0) a.lse_out[orow_out] = tot > 0.f ? M + logf(tot) : -INFINITY;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows have landed
+  __syncthreads();                                  // u row and all W rows visible
+
+  // ---- 4. o[r, h, v] = W^UV_i[v] . u (two threads per output) ----
+  const int v = tid >> 1, half = tid & 1;
+  if (v < dv) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+    const uint32_t wb = lds_addr(sm.w), ub = lds_addr(sm.u);
+    float d = 0.f;
+#pragma unroll 8
+    for (int x = 0; x < kDC / 16; ++x) {
+      const int xc = (kDC / 16) * half + x;  // 16-byte chunk of channels
+      const u32x4 wv = *(lds_u4*)(uintptr_t)(wb + chunk_off(v, xc));
+      const u32x4 uv = *(lds_u4*)(uintptr_t)(ub + xc * 16);
+      const uint32_t wa[4] = {wv[0], wv[1], wv[2], wv[3]}, ua[4] = {uv[0], uv[1], uv[2], uv[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(ua[e] << 16), d);
+        d = fmaf(__uint_as_float(wa[e] & 0xffff0000u), __uint_as_float(ua[e] & 0xffff0000u), d);
+      }
+    }
+    d += __shfl_xor(d, 1, 64);
+    if (half == 0) static_cast<__bf16*>(a.out)[orow_out * dv + v] = (__bf16)d;
+  }
+}
+
 }  // namespace
 
 bool combine_out_proj_supported(const CombineProjArgs& a) {
@@ -282,9 +438,17 @@ hipError_t launch_combine_out_proj(const CombineProjArgs& a, hipStream_t st) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(combine_out_proj_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(Smem)));
     if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(combine_out_proj_row_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(RowSmem)));
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int R = a.batch * a.n_q;
+  if (R <= kMaxRowModeRows) {  // few rows: one workgroup per (head, row)
+    hipLaunchKernelGGL(combine_out_proj_row_kernel, dim3(unsigned(a.H) * unsigned(R)), dim3(kNT),
+                       sizeof(RowSmem), st, a);
+    return hipGetLastError();
+  }
   const unsigned n = unsigned(a.H) * unsigned((R + kRows - 1) / kRows);
   hipLaunchKernelGGL(combine_out_proj_kernel, dim3(n), dim3(kNT), sizeof(Smem), st, a);
   return hipGetLastError();
