@@ -45,8 +45,9 @@ struct Smem {
 };
 // the plan scratch, slot tables and staged lengths live in the u tile until
 // it is written
-constexpr int kMaxSeq = kRows + 1;
-constexpr int kLensOff = 5632;        // 256-byte aligned, past scratch and tables
+constexpr int kMaxGroups = 8;         // row groups per workgroup (W^UV_i loaded once for all)
+constexpr int kMaxSeq = kMaxGroups * kRows + 1;
+constexpr int kLensOff = 7424;        // 256-byte aligned, past scratch and tables
 constexpr int kMaxLensLds = 4096;     // sequences whose lengths are staged in LDS
 static_assert(sizeof(PlanScratch<kNT>) + 2 * kMaxSeq * sizeof(int) <= kLensOff &&
                   kLensOff + kMaxLensLds * 4 <= kRows * kRowBytes,
@@ -76,8 +77,10 @@ MLA_DEV void load_w_rows(unsigned char* dst, const void* w_uv, int h, int dv, in
   }
 }
 
+// One workgroup per (head, gpw consecutive groups of 32 rows): W^UV_i is
+// loaded once and serves every group.
 __global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void combine_out_proj_kernel(CombineProjArgs a) {
+void combine_out_proj_kernel(CombineProjArgs a, int gpw) {
   extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int lane = threadIdx.x % kWave;
@@ -85,11 +88,13 @@ void combine_out_proj_kernel(CombineProjArgs a) {
   const int g = lane / 32, m = lane % 32;
   const int R = a.batch * a.n_q, H = a.H, dv = a.d_v;
   const int ngroups = (R + kRows - 1) / kRows;
+  const int nblk = (ngroups + gpw - 1) / gpw;  // workgroups per head
   // consecutive logical ids share an XCD (workgroups are dealt round-robin)
   const int NB = gridDim.x, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
   const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;
-  const int h = logical / ngroups, r0 = (logical % ngroups) * kRows;
-  const int nrows = min(kRows, R - r0);
+  const int h = logical / nblk, gb = logical % nblk;
+  const int R0 = gb * gpw * kRows, Rend = min(R, R0 + gpw * kRows);
+  const int ngr = (Rend - R0 + kRows - 1) / kRows;  // groups of this workgroup
 
 
   // ---- 0. lengths (wave 0) and W^UV_i (all waves) into LDS ----
@@ -107,31 +112,39 @@ void combine_out_proj_kernel(CombineProjArgs a) {
   load_w_rows(sm.w, a.w_uv, h, dv, wave, lane);
   lds_barrier();
 
-  // ---- 1. first slot and piece count of this group's sequences ----
+  // ---- 1. first slot and piece count of this workgroup's sequences ----
   PlanScratch<kNT>& ps = *reinterpret_cast<PlanScratch<kNT>*>(sm.u);
   int* t_slot0 = reinterpret_cast<int*>(sm.u + sizeof(PlanScratch<kNT>));
   int* t_np = t_slot0 + kMaxSeq;
-  const int b_lo = r0 / a.n_q;
-  const int nb = (r0 + nrows - 1) / a.n_q - b_lo + 1;
+  const int b_lo = R0 / a.n_q;
+  const int nb = (Rend - 1) / a.n_q - b_lo + 1;
   if (lens_in_lds)
     plan_slots<kNT>((lds_i32*)(uintptr_t)lds_addr(sm.u + kLensOff), a.batch, a.block_size, a.G, b_lo, nb, ps,
                     t_slot0, t_np);
   else
     plan_slots<kNT>(a.seq_lens, a.batch, a.block_size, a.G, b_lo, nb, ps, t_slot0, t_np);
-  int slot0[kRowsPerWave], np[kRowsPerWave], maxnp = 0;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int r = wave * kRowsPerWave + i;
-    slot0[i] = 0;
-    np[i] = 0;
-    if (r < nrows) {
-      const int bi = (r0 + r) / a.n_q - b_lo;
-      slot0[i] = __builtin_amdgcn_readfirstlane(t_slot0[bi]);
-      np[i] = __builtin_amdgcn_readfirstlane(t_np[bi]);
-      maxnp = max(maxnp, np[i]);
+  // lane l keeps the table entries of this wave's row l % 8 in group l / 8
+  static_assert(kMaxGroups * kRowsPerWave <= kWave, "one row per lane");
+  int l_slot0 = 0, l_np = 0;
+  {
+    const int row = R0 + (lane / kRowsPerWave) * kRows + wave * kRowsPerWave + lane % kRowsPerWave;
+    if (lane / kRowsPerWave < ngr && row < Rend) {
+      const int bi = row / a.n_q - b_lo;
+      l_slot0 = t_slot0[bi];
+      l_np = t_np[bi];
     }
   }
   lds_barrier();  // the tables are read; the u tile may be overwritten
+
+  for (int k = 0; k < ngr; ++k) {
+  const int r0 = R0 + k * kRows, nrows = min(kRows, R - r0);
+  int slot0[kRowsPerWave], np[kRowsPerWave], maxnp = 0;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    slot0[i] = __builtin_amdgcn_readlane(l_slot0, k * kRowsPerWave + i);
+    np[i] = __builtin_amdgcn_readlane(l_np, k * kRowsPerWave + i);
+    maxnp = max(maxnp, np[i]);
+  }
 
   // ---- 2. merge the pieces of this wave's 8 rows (lane = 8 channels) ----
   float M[kRowsPerWave], wsum[kRowsPerWave], acc[kRowsPerWave][8];
@@ -157,12 +170,12 @@ void combine_out_proj_kernel(CombineProjArgs a) {
   static_assert(kRowsPerWave * kPC <= kWave, "one lse per lane");
   // lane l < 32 fetches the lse of (row l / kPC, piece s0 + l % kPC)
   const int li = min(lane / kPC, kRowsPerWave - 1), lsp = lane % kPC;
-  int l_np = 0;
+  int ln_np = 0;
   const float* l_lrow = lrow[0];
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i)
     if (li == i) {
-      l_np = np[i];
+      ln_np = np[i];
       l_lrow = lrow[i];
     }
   for (int s0 = 0; s0 < maxnp; s0 += kPC) {
@@ -172,8 +185,8 @@ void combine_out_proj_kernel(CombineProjArgs a) {
     // for every load before issuing the next): a piece past the row's count
     // reads the row's last piece (a row with none reads slot 0) and is masked
     // below by lse = -inf.
-    const int lp = max(0, min(s0 + lsp, l_np - 1));
-    const float lse_l = l_lrow[l_np > 0 ? size_t(lp) * pstride : 0];
+    const int lp = max(0, min(s0 + lsp, ln_np - 1));
+    const float lse_l = l_lrow[ln_np > 0 ? size_t(lp) * pstride : 0];
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i)
 #pragma unroll
@@ -240,7 +253,7 @@ void combine_out_proj_kernel(CombineProjArgs a) {
 
   // ---- 3. o[rows, h, 32w..32w+31] = u . W^T on MFMA ----
   const int v0 = wave * 32;
-  if (v0 >= dv) return;
+  if (v0 < dv) {
   f32x16 o = {};
   const uint32_t ub = lds_addr(sm.u), wb = lds_addr(sm.w);
   auto afrag = [&](int s) { return *(lds_bf16x8*)(uintptr_t)(ub + chunk_off(m, 2 * s + g)); };
@@ -263,9 +276,12 @@ void combine_out_proj_kernel(CombineProjArgs a) {
   // lane (g, m) holds rows 8*(k/4) + 4*g + k%4 of column v0 + m
   __bf16* out = static_cast<__bf16*>(a.out);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int r = 8 * (k / 4) + 4 * g + (k % 4);
-    if (r < nrows) out[(size_t(r0 + r) * H + h) * dv + v0 + m] = (__bf16)o[k];
+  for (int q = 0; q < 16; ++q) {
+    const int r = 8 * (q / 4) + 4 * g + (q % 4);
+    if (r < nrows) out[(size_t(r0 + r) * H + h) * dv + v0 + m] = (__bf16)o[q];
+  }
+  }
+  lds_barrier();  // every wave is done with the u tile before the next group writes it
   }
 }
 
@@ -449,8 +465,12 @@ hipError_t launch_combine_out_proj(const CombineProjArgs& a, hipStream_t st) {
                        sizeof(RowSmem), st, a);
     return hipGetLastError();
   }
-  const unsigned n = unsigned(a.H) * unsigned((R + kRows - 1) / kRows);
-  hipLaunchKernelGGL(combine_out_proj_kernel, dim3(n), dim3(kNT), sizeof(Smem), st, a);
+  // enough row groups per workgroup to keep about 256 workgroups (one per
+  // compute unit) while reading each head's W^UV_i as few times as possible
+  const int ngroups = (R + kRows - 1) / kRows;
+  const int gpw = max(1, min(kMaxGroups, ngroups * a.H / 256));
+  const unsigned n = unsigned(a.H) * unsigned((ngroups + gpw - 1) / gpw);
+  hipLaunchKernelGGL(combine_out_proj_kernel, dim3(n), dim3(kNT), sizeof(Smem), st, a, gpw);
   return hipGetLastError();
 }
 
