@@ -76,7 +76,8 @@ def traffic_from_profile(kernel_src: str, workload: str):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_hash") != source_hash(kernel_src):
+    # the kernel's own file plus the shared headers it is compiled with
+    if d.get("source_hash") != source_hash(kernel_src, "mla_common.h", "mla_internal.h"):
         return None
     return d.get("hbm_bytes_per_launch")
 
