@@ -3,6 +3,7 @@
 
 A step is one pass of the whole hot path on one batch of synthetic input:
   mla_cache_append  (B new tokens: W^DKV / W^KR projection, RoPE, paged write)
+  mla_query_absorb  (q~ = W^UK^T q^C and RoPE(q^R) for every query and head)
   mla_decode        (split-KV attention over the latent cache, all heads)
   mla_decode_combine_out_proj
                     (log-sum-exp merge of the splits, then the per-head W^UV
@@ -12,7 +13,7 @@ Default workload: DeepSeek-V3 shape, bf16, B=64 sequences of L=4096 cached
 tokens, one query token each, H=128, d_c=512, d_R=64, block 64, shuffled page
 table.  Inputs are resident in HBM before timing; several copies of the pool
 are rotated so the 256 MB last-level cache cannot serve the cache stream.
-The timed region launches the four calls per step with only a start and a
+The timed region launches the calls of a step with only a start and a
 stop event (--graph replays one captured HIP graph per step instead); the
 per-kernel times, and the decode time the roofline uses, come from a second
 pass of the same steps with an event around every call.
@@ -135,7 +136,12 @@ def main():
             pools.append(rows.to(torch.bfloat16).view(nblk, bs, D))
             scales.append(None)
         del rows
-    q = W.absorbed_queries(cfg, seed=cfg.seed + 20, device=dev).to(torch.bfloat16)
+    # queries: per head the content part q^C and the un-rotated RoPE part q^R,
+    # N(0, 1), absorbed on the GPU every step (W^UK ~ N(0, 1/d_c))
+    q_in = W.normal((B, n_q, H, d.d_nope + d.d_rope), cfg.seed + 20, device=dev, dtype=torch.bfloat16)
+    w_uk = W.normal((H, d.d_nope, d.d_latent), cfg.seed + 34, std=1 / math.sqrt(d.d_latent),
+                    device=dev, dtype=torch.bfloat16)
+    q = torch.empty(B, n_q, H, D, dtype=torch.bfloat16, device=dev)
     table_t = torch.from_numpy(table).to(dev)
     lens_t = torch.from_numpy(lens).to(dev)
     # append inputs: the n_q newest tokens of every sequence
@@ -161,6 +167,7 @@ def main():
         pool, sc = pools[i % n_copies], scales[i % n_copies]
         head = [
             lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc, aws),
+            lambda: M.mla_query_absorb(dims, q_in, positions, w_uk, q),
             lambda: M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G),
         ]
         if args.separate:
@@ -170,14 +177,15 @@ def main():
             ]
         return head + [lambda: M.mla_decode_combine_out_proj(dims, ws, lens_t, w_uv, o, B, n_q, None,
                                                              None, G)]
-    names = ["append", "decode"] + (["combine", "out_proj"] if args.separate else ["combine_out_proj"])
+    names = ["append", "query_absorb", "decode"] + (["combine", "out_proj"] if args.separate
+                                                     else ["combine_out_proj"])
 
     for i in range(args.warmup):
         for c in calls(i):
             c()
     torch.cuda.synchronize()
 
-    # --graph: the four calls of a step (per pool copy) are captured once into
+    # --graph: the calls of a step (per pool copy) are captured once into
     # one HIP graph (they allocate nothing and record no memsets) and a step
     # replays it.  Default: the calls are launched directly.
     if args.graph:
@@ -227,7 +235,7 @@ def main():
     torch.cuda.synchronize()
     per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
     k_ms = per.mean(axis=0)
-    decode_ms = float(k_ms[1])
+    decode_ms = float(k_ms[names.index("decode")])
 
     # ---- roofline of the dominant kernel (decode) ---------------------------
     bytes_alg = kv_tokens * BYTES_PER_KV_TOKEN[cfg.cache_dtype] + B * n_q * H * D * 2
@@ -247,7 +255,7 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, pools[0], scales[0], table, lens, q, h, w_dkv, w_kr, w_uv,
+        cpu = cpu_baseline(cfg, pools[0], scales[0], table, lens, q_in, w_uk, h, w_dkv, w_kr, w_uv,
                            args.cpu_seconds)
 
     out = {
@@ -273,10 +281,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, pool, sc, table, lens, q, h, w_dkv, w_kr, w_uv, seconds):
+def cpu_baseline(cfg, pool, sc, table, lens, q_in, w_uk, h, w_dkv, w_kr, w_uv, seconds):
     """The oracle as it stands (float64 NumPy), on a bounded sample of the same
-    workload: the first few sequences' decode plus their append rows and
-    up-projection, repeated until about ``seconds`` of CPU work."""
+    workload: the first few sequences' append rows, query absorption, decode
+    and up-projection, repeated until about ``seconds`` of CPU work."""
     import torch
     from oracle import mla_oracle as O
 
@@ -300,14 +308,16 @@ def cpu_baseline(cfg, pool, sc, table, lens, q, h, w_dkv, w_kr, w_uv, seconds):
     def f64(t):
         return O.bf16_bits_to_f64(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
 
-    qh = f64(q[:n_seq])
+    qin = f64(q_in[:n_seq])
     hh = f64(h[:n_seq * cfg.n_q])
-    wd, wk, wu = f64(w_dkv), f64(w_kr), f64(w_uv)
+    wd, wk, wu, wq = f64(w_dkv), f64(w_kr), f64(w_uv), f64(w_uk)
     scale = O.softmax_scale(d.d_nope, d.d_rope)
     pos = (lens[:n_seq].repeat(cfg.n_q) - 1).astype(np.int64)
+    qpos = (lens[:n_seq, None] - cfg.n_q + np.arange(cfg.n_q)[None, :]).astype(np.int64)
     reps, t_start = 0, time.perf_counter()
     while True:
         O.kv_rows(hh, wd, wk, pos)
+        qh = O.absorb_query(qin[..., :d.d_nope], qin[..., d.d_nope:], wq, qpos)
         res = O.decode(qh, host_pool, table, lens, bs, d.d_latent, scale, batch_ids=ids)
         O.out_proj(np.concatenate([res[b][0] for b in ids]), wu)
         reps += 1
@@ -318,7 +328,8 @@ def cpu_baseline(cfg, pool, sc, table, lens, q, h, w_dkv, w_kr, w_uv, seconds):
     return {"value": round(reps * int(lens[:n_seq].sum()) / el, 1), "unit": "KV-tokens/s",
             "cores": cores, "kind": "oracle",
             "sample": f"{n_seq} of {cfg.batch} sequences ({int(lens[:n_seq].sum())} KV-tokens), "
-                      f"append rows + absorbed decode + W^UV in float64 NumPy, {reps} repetitions "
+                      f"append rows + query absorption + absorbed decode + W^UV in float64 NumPy, "
+                      f"{reps} repetitions "
                       f"in {el:.1f} s"}
 
 

@@ -83,8 +83,9 @@ typedef struct mla_dims {
   int32_t flags;       /* bitwise OR of MLA_FLAG_*; 0 for defaults */
 } mla_dims;
 
-/* Use the generic VALU decode kernel even where the MFMA kernel applies
- * (an independent second implementation, for cross-checks). */
+/* Use the generic VALU kernels (decode, query absorption) even where the
+ * MFMA kernels apply (an independent second implementation, for
+ * cross-checks). */
 #define MLA_FLAG_GENERIC_DECODE 1
 
 int mla_abi_version(void);
@@ -128,6 +129,28 @@ int mla_cache_append(const mla_dims *dims, const void *h, int32_t n_tokens, int3
                      const int32_t *positions, const int32_t *page_table,
                      int32_t max_blocks_per_seq, void *cache, float *cache_scales,
                      void *workspace, size_t workspace_bytes, mla_stream_t stream);
+
+/*
+ * mla_query_absorb -- matrix-absorbed query of every (row, head).
+ * [MLA-93] Core Mechanics 3 (decoupled RoPE and absorption of W^UK into the
+ * query) and its decoding section: per head i,
+ *   q~_i  = (W^UK_i)^T q^C_i                      in R^{d_latent}
+ *   q^R_i = RoPE(q^R_i, position)                 (rotate-half, base rope_base)
+ * written packed as [q~_i ; q^R_i], the query layout mla_decode reads.
+ *   q_in      [rows][num_heads][d_nope + d_rope] act_dtype: per head the
+ *             content part q^C then the un-rotated RoPE part (the head-major
+ *             split of the query projection)
+ *   positions [rows] int32 >= 0: the position each row's query sits at
+ *   w_uk      [num_heads][d_nope][d_latent] act_dtype (k^C_i = W^UK_i c)
+ *   q_out     [rows][num_heads][d_latent + d_rope] act_dtype; must not
+ *             overlap q_in
+ * rows = batch * n_q in mla_decode's order.  fp32 accumulation; RoPE angles in
+ * fp64 with cos/sin rounded to fp32 (as in mla_cache_append); bf16 outputs
+ * round to nearest even.  bf16 with d_nope a multiple of 16 and d_latent of
+ * 128 runs on the matrix cores; other shapes on a VALU kernel.
+ */
+int mla_query_absorb(const mla_dims *dims, const void *q_in, const int32_t *positions,
+                     const void *w_uk, void *q_out, int32_t rows, mla_stream_t stream);
 
 /*
  * Split-KV decode (mla_decode + mla_decode_combine).

@@ -27,7 +27,7 @@ ERR_HIP = -4
 EXPORTS = ("mla_abi_version", "mla_last_error", "mla_device_cu_count",
            "mla_cache_append_workspace_size", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_combine", "mla_out_proj",
-           "mla_decode_combine_out_proj")
+           "mla_decode_combine_out_proj", "mla_query_absorb")
 
 
 class MlaError(RuntimeError):
@@ -86,8 +86,9 @@ def lib():
         L.mla_out_proj.argtypes = [D, _P, _I, _P, _P, _P]
         L.mla_decode_combine_out_proj.argtypes = [D, _P, ctypes.c_size_t, _I, _I, _P, _I, _P, _P,
                                                   _P, _P, _P]
+        L.mla_query_absorb.argtypes = [D, _P, _P, _P, _P, _I, _P]
         for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj",
-                  "mla_decode_combine_out_proj"):
+                  "mla_decode_combine_out_proj", "mla_query_absorb"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,3 +173,11 @@ def mla_out_proj(dims, u, w_uv, out, stream=None):
     """u [rows, H, d_latent]; w_uv [H, d_v, d_latent]; out [rows, H, d_v]."""
     _check(lib().mla_out_proj(ctypes.byref(dims), _ptr(u), u.shape[0], _ptr(w_uv), _ptr(out),
                               _stream(stream)))
+
+
+def mla_query_absorb(dims, q_in, positions, w_uk, q_out, stream=None):
+    """q_in [rows, H, d_nope + d_rope] (any leading shape whose product is rows);
+    positions [rows] int32; w_uk [H, d_nope, d_latent]; q_out [rows, H, d_latent + d_rope]."""
+    rows = q_in.numel() // (dims.num_heads * (dims.d_nope + dims.d_rope))
+    _check(lib().mla_query_absorb(ctypes.byref(dims), _ptr(q_in), _ptr(positions), _ptr(w_uk),
+                                  _ptr(q_out), rows, _stream(stream)))

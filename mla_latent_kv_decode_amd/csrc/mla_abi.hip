@@ -267,6 +267,40 @@ int mla_decode_combine(const mla_dims* d, const void* workspace, size_t workspac
   return ok();
 }
 
+int mla_query_absorb(const mla_dims* d, const void* q_in, const int32_t* positions, const void* w_uk,
+                     void* q_out, int32_t rows, mla_stream_t stream) {
+  if (int e = check_dims(d, false)) return e;
+  if (d->d_nope < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "query absorption needs d_nope >= 1");
+  if (rows < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "rows=%d", rows);
+  if (rows == 0) return ok();
+  if (!q_in || !positions || !w_uk || !q_out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t ae = elem_bytes(d->act_dtype);
+  if (!aligned(q_in, ae) || !aligned(w_uk, ae) || !aligned(q_out, ae) || !aligned(positions, 4))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  const size_t in_bytes = size_t(rows) * d->num_heads * (d->d_nope + d->d_rope) * ae;
+  const size_t out_bytes = size_t(rows) * d->num_heads * (d->d_latent + d->d_rope) * ae;
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(q_in), o0 = reinterpret_cast<uintptr_t>(q_out);
+  if (i0 < o0 + out_bytes && o0 < i0 + in_bytes)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q_out overlaps q_in");
+  mla::QueryArgs a;
+  a.q_in = q_in;
+  a.positions = positions;
+  a.w_uk = w_uk;
+  a.q_out = q_out;
+  a.rows = rows;
+  a.H = d->num_heads;
+  a.d_nope = d->d_nope;
+  a.d_rope = d->d_rope;
+  a.d_latent = d->d_latent;
+  a.act_dtype = d->act_dtype;
+  a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  const bool mfma = !(d->flags & MLA_FLAG_GENERIC_DECODE) && mla::query_absorb_mfma_supported(a);
+  hipError_t e = mfma ? mla::launch_query_absorb_mfma(a, static_cast<hipStream_t>(stream))
+                      : mla::launch_query_absorb_generic(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "query_absorb launch");
+  return ok();
+}
+
 int mla_out_proj(const mla_dims* d, const void* u, int32_t rows, const void* w_uv, void* out,
                  mla_stream_t stream) {
   if (int e = check_dims(d, false)) return e;

@@ -54,6 +54,20 @@ struct AppendArgs {
   float rope_base;
 };
 
+struct QueryArgs {
+  const void* q_in;        // [rows][H][d_nope + d_rope]
+  const int32_t* positions;
+  const void* w_uk;        // [H][d_nope][d_latent]
+  void* q_out;             // [rows][H][d_latent + d_rope]
+  int rows, H, d_nope, d_rope, d_latent;
+  int act_dtype;
+  float rope_base;
+};
+
+bool query_absorb_mfma_supported(const QueryArgs& a);
+hipError_t launch_query_absorb_mfma(const QueryArgs& a, hipStream_t st);
+hipError_t launch_query_absorb_generic(const QueryArgs& a, hipStream_t st);
+
 struct OutProjArgs {
   const void* u;           // [rows][H][d_latent]
   const void* w;           // [H][d_v][d_latent]

@@ -130,3 +130,23 @@ def test_combine_out_proj_validates(L):
     ws_odd = L.mla_decode_workspace_size(odd, 4, 1, 8)
     assert call(ctypes.byref(odd), ws_bytes=ws_odd) == L.ERR_UNSUPPORTED
     assert "u_out" in lib.mla_last_error().decode()
+
+
+def test_query_absorb_validates(L):
+    lib = L.lib()
+    d = _dims(L)
+    call = lambda dims, q=FAKE, pos=FAKE, w=FAKE, out=FAKE * 4, rows=2: \
+        lib.mla_query_absorb(dims, q, pos, w, out, rows, None)
+    assert call(None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), q=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), pos=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), w=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), out=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), rows=-1) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), rows=0) == L.OK          # nothing to do, nothing touched
+    assert call(ctypes.byref(d), q=FAKE + 1) == L.ERR_INVALID_ARGUMENT  # misaligned bf16
+    # q_out overlapping q_in
+    assert call(ctypes.byref(d), out=FAKE + 256) == L.ERR_INVALID_ARGUMENT
+    assert "overlap" in lib.mla_last_error().decode()
+    no_nope = _dims(L, d_nope=0, softmax_scale=0.1)
+    assert call(ctypes.byref(no_nope)) == L.ERR_INVALID_ARGUMENT

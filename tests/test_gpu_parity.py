@@ -55,6 +55,11 @@ def test_tiny_end_to_end_fp32():
     o_ref = O.out_proj(u_ref, w_uv)
     # GPU: contiguous cache = identity page table over 2 blocks of 64
     dims = dims_of(cfg)
+    # query: the projection W^Q h is the caller's (torch); absorption + q-RoPE on the GPU
+    q_full = (_t(h[64:65], torch.float32) @ _t(w_q, torch.float32).T).view(1, H, d.d_nope + d.d_rope)
+    q_gpu = torch.empty(1, H, d.row, device="cuda")
+    M.mla_query_absorb(dims, q_full.contiguous(), torch.tensor([64], dtype=torch.int32, device="cuda"),
+                       _t(w_uk, torch.float32), q_gpu)
     cache = torch.full((2, 64, d.row), float("nan"), device="cuda")
     table = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
     M.mla_cache_append(dims, _t(h, torch.float32), _t(w_dkv, torch.float32),
@@ -62,7 +67,7 @@ def test_tiny_end_to_end_fp32():
                        _t(pos, torch.int32), table, cache)
     lens = torch.tensor([65], dtype=torch.int32, device="cuda")
     ws = torch.empty(M.mla_decode_workspace_size(dims, 1, 1, 0), dtype=torch.uint8, device="cuda")
-    qd = _t(q, torch.float32).view(1, 1, H, d.row)
+    qd = q_gpu.view(1, 1, H, d.row)
     M.mla_decode(dims, qd, cache, None, table, lens, ws)
     u = torch.empty(1, 1, H, d.d_latent, device="cuda")
     lse = torch.empty(1, 1, H, device="cuda")
@@ -72,11 +77,69 @@ def test_tiny_end_to_end_fp32():
     torch.cuda.synchronize()
     got_rows = cache.view(-1, d.row)[:65].cpu().numpy().astype(np.float64)
     assert rel_l2(got_rows, rows) <= 1e-6
+    assert rel_l2(q_gpu.cpu().numpy()[0].astype(np.float64), q) <= 1e-6
     assert rel_l2(u.cpu().numpy()[0], u_ref) <= 1e-5
     assert max_abs(lse.cpu().numpy()[0], lse_ref) <= 1e-5
     assert rel_l2(o.cpu().numpy(), o_ref) <= 1e-5
     assert max_abs(o.cpu().numpy(), o_ref) <= 2e-2
     assert torch.isnan(cache.view(-1, d.row)[65:]).all(), "slots past the sequence were written"
+
+
+# --------------------------------------------------------------------------
+# query absorption + q-RoPE (mla_query_absorb)
+# --------------------------------------------------------------------------
+def _query_case(H, d_nope, d_rope, d_latent, rows, seed, dtype):
+    q_in = W.normal((rows, H, d_nope + d_rope), seed, device="cuda").to(dtype)
+    w_uk = W.normal((H, d_nope, d_latent), seed + 1, std=1 / math.sqrt(d_latent), device="cuda").to(dtype)
+    pos = np.random.default_rng(seed + 2).integers(0, 131072, size=rows).astype(np.int32)
+    pos[0] = 0
+    pos[-1] = 131071   # long-context angles: the fp64 angle matters here
+    ref = O.absorb_query(to_f64(q_in[..., :d_nope]), to_f64(q_in[..., d_nope:]), to_f64(w_uk), pos)
+    return q_in, w_uk, torch.from_numpy(pos).cuda(), ref
+
+
+@pytest.mark.parametrize("rows", [1, 64, 70])
+def test_query_absorb_v3_bf16(rows):
+    import mla_latent_kv_decode_amd as M
+    d = W.V3
+    dims = dims_of(W.CONFIGS["v3"])
+    q_in, w_uk, pos, ref = _query_case(d.num_heads, d.d_nope, d.d_rope, d.d_latent, rows, 40 + rows,
+                                       torch.bfloat16)
+    out = torch.full((rows, d.num_heads, d.row), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.mla_query_absorb(dims, q_in, pos, w_uk, out)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2
+    # the rotation itself: bf16 in, fp32 arithmetic, one bf16 rounding out
+    assert rel_l2(got[..., d.d_latent:], ref[..., d.d_latent:]) <= 4e-3
+
+
+def test_query_absorb_generic_fp32_tight():
+    import mla_latent_kv_decode_amd as M
+    d = W.TINY
+    dims = dims_of(W.CONFIGS["tiny"])
+    q_in, w_uk, pos, ref = _query_case(d.num_heads, d.d_nope, d.d_rope, d.d_latent, 37, 60, torch.float32)
+    out = torch.empty(37, d.num_heads, d.row, device="cuda")
+    M.mla_query_absorb(dims, q_in, pos, w_uk, out)
+    torch.cuda.synchronize()
+    assert rel_l2(out.cpu().numpy().astype(np.float64), ref) <= 1e-6
+
+
+def test_query_absorb_mfma_agrees_with_generic():
+    import mla_latent_kv_decode_amd as M
+    d = W.V3
+    q_in, w_uk, pos, _ = _query_case(d.num_heads, d.d_nope, d.d_rope, d.d_latent, 50, 70, torch.bfloat16)
+    outs = []
+    for flags in (0, M.FLAG_GENERIC_DECODE):
+        out = torch.empty(50, d.num_heads, d.row, dtype=torch.bfloat16, device="cuda")
+        M.mla_query_absorb(dims_of(W.CONFIGS["v3"], flags), q_in, pos, w_uk, out)
+        outs.append(to_f64(out))
+    torch.cuda.synchronize()
+    # same products, summed in another order: at most a bf16 rounding apart
+    assert rel_l2(outs[0], outs[1]) <= 2e-3
+    # the RoPE part is the same arithmetic on both paths (up to fma contraction)
+    assert rel_l2(outs[0][..., d.d_latent:], outs[1][..., d.d_latent:]) <= 1e-4
 
 
 # --------------------------------------------------------------------------
