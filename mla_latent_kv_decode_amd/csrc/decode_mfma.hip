@@ -98,6 +98,7 @@ struct Smem {
   // for the fp8 cache, staging buffer i follows the three step buffers
   alignas(128) unsigned char lds[kLdsBytes];
   PlanScratch<kNT> plan;
+  alignas(16) int32_t lens[256];  // window of sequence lengths for the plan
 };
 
 // Wait until at most N of this wave's vector-memory operations are pending.
@@ -315,7 +316,27 @@ void decode_mfma_kernel(DecodeArgs a) {
   };
   const int loff = load_lane_off(lane, wave & 1);
 
-  plan_for_each_piece<kNT>(a.seq_lens, a.batch, kBS, a.G, part, sm.plan,
+  // Speculative Q: with equal lengths, partition `part`'s first piece belongs
+  // to sequence part * B / G, so that sequence's Q starts streaming into the
+  // step buffers now and the plan is computed while it is in flight.  The
+  // plan reads its lengths from an LDS window whose loads wave 0 issues
+  // before the Q loads (so waiting for them never waits for Q).  A wrong
+  // guess costs only the load: the piece then issues its own, which
+  // completes later and overwrites it.
+  LdsLensWindow lens{lds_addr(reinterpret_cast<const unsigned char*>(sm.lens)), a.seq_lens, a.batch, 0};
+  const int b_pre = int(int64_t(part) * a.batch / a.G);
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const unsigned char* qblk = static_cast<const unsigned char*>(a.q) + (size_t(b) * a.n_q + j) * kH * kRowBytes;
+#pragma unroll
+    for (int t = 0; t < kNT / kWave; ++t) load_step(bbuf(t), qblk + t * kStepBytes, kStep, wave, loff);
+  };
+  if (wave == 0) lens_window_issue(lens, 0);
+  load_q(b_pre);
+  if (wave == 0) wait_vm<kNBuf * kLoadsPerWave>();  // the lengths, not the Q loads behind them
+  lds_barrier();
+  bool q_pre = true;  // the prefetched Q may still serve the first piece
+
+  plan_for_each_piece<kNT>(lens, a.batch, kBS, a.G, part, sm.plan,
                            [&](int b_, int ulo_, int uhi_, int slot_, int L_) {
     // piece bounds come from LDS: tell the compiler they are wave-uniform
     const int b = __builtin_amdgcn_readfirstlane(b_), ulo = __builtin_amdgcn_readfirstlane(ulo_);
@@ -353,12 +374,8 @@ void decode_mfma_kernel(DecodeArgs a) {
     // own direct loads and layout (wave t's block into buffer t), and each
     // wave reads its fragments exactly like K fragments: whole-row loads
     // instead of 16-byte pieces of 32 rows per instruction.
-    {
-      const unsigned char* qblk = static_cast<const unsigned char*>(a.q) +
-                                  (size_t(b) * a.n_q + j) * kH * kRowBytes;
-#pragma unroll
-      for (int t = 0; t < kNT / kWave; ++t) load_step(bbuf(t), qblk + t * kStepBytes, kStep, wave, loff);
-    }
+    if (!(q_pre && b == b_pre)) load_q(b);
+    q_pre = false;
     wait_vm<0>();
     step_barrier();
     bf16x8 qf[kQK];
@@ -584,6 +601,7 @@ void decode_mfma_kernel(DecodeArgs a) {
                                   orow + r * (kDC / 8));
     step_barrier();  // every wave is done with the stage before a next piece loads into it
   });
+  wait_vm<0>();  // a prefetched Q no piece used must land before the workgroup's LDS is released
 }
 
 }  // namespace

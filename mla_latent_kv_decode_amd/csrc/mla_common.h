@@ -222,18 +222,59 @@ struct PlanScratch {
   int red[2 * NT / kWave];
 };
 
+// Where the plan reads the sequence lengths from: a global pointer, an LDS
+// copy of all of them, or an LDS window of one chunk of NT sequences that is
+// filled by a direct load when the plan moves to that chunk
+// (lens_stage(src, c) is called by every thread at each chunk start).
+typedef __attribute__((address_space(3))) const int32_t lds_len_t;
+MLA_DEV void lens_stage(const int32_t*, int) {}
+MLA_DEV int lens_get(const int32_t* p, int b) { return p[b]; }
+MLA_DEV void lens_stage(lds_len_t*, int) {}
+MLA_DEV int lens_get(lds_len_t* p, int b) { return p[b]; }
+struct LdsLensWindow {
+  uint32_t lds;          // LDS byte address of a 1 KB window (256 lengths)
+  const int32_t* g;      // the lengths in global memory
+  int B;
+  int cur;               // first sequence of the staged chunk, -1 if none
+};
+// Wave 0 issues the four direct dword loads (64 lengths each; only 4-byte
+// alignment needed) of the window starting at sequence c; lengths past B read
+// as 0.  The caller waits for them.
+MLA_DEV void lens_window_issue(const LdsLensWindow& w, int c) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(w.g + c), (short)0, min(w.B - c, 256) * 4, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(int(threadIdx.x) * 4), "s"(r), "s"(i * 256), "{m0}"(w.lds + i * 256)
+                 : "memory");
+}
+MLA_DEV void lens_stage(LdsLensWindow& w, int c) {
+  if (c == w.cur) return;  // uniform
+  lds_barrier();           // nobody reads the previous window any more
+  if (threadIdx.x < kWave) {
+    lens_window_issue(w, c);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  lds_barrier();
+  w.cur = c;
+}
+MLA_DEV int lens_get(const LdsLensWindow& w, int b) { return ((lds_len_t*)(uintptr_t)w.lds)[b - w.cur]; }
+
 // T = total units.  Also returns the first chunk's per-thread length,
 // exclusive unit prefix and unit total, which the callers reuse (the whole
 // plan when B <= NT).
-// seq_lens may be a global pointer or an LDS copy (LenP = its pointer type).
 template <int NT, class LenP>
-MLA_DEV int plan_total_units(LenP seq_lens, int B, int bs, PlanScratch<NT>& sc, int* len0,
+MLA_DEV int plan_total_units(LenP&& seq_lens, int B, int bs, PlanScratch<NT>& sc, int* len0,
                              int* S0, int* tot0) {
+  static_assert(NT <= 256, "one length window holds 256 sequences");
   int T = 0;
   *len0 = *S0 = *tot0 = 0;
   for (int c = 0; c < B; c += NT) {
     const int b = c + threadIdx.x;
-    const int len = b < B ? seq_lens[b] : 0;
+    lens_stage(seq_lens, c);
+    const int len = b < B ? lens_get(seq_lens, b) : 0;
     int tot;
     const int S = block_excl_scan<NT>(units_of(len, bs), sc.red, &tot);
     if (c == 0) { *len0 = len; *S0 = S; *tot0 = tot; }
@@ -272,7 +313,7 @@ MLA_DEV int plan_chunk(int c, int len, int S, int bs, const PartGrid& pg, int g,
 // workgroup-uniform values stay live across f (the chunk-0 list is built
 // before the loop), so f gets the whole register file.
 template <int NT, class LenP, class F>
-MLA_DEV void plan_for_each_piece(LenP seq_lens, int B, int bs, int G, int g,
+MLA_DEV void plan_for_each_piece(LenP&& seq_lens, int B, int bs, int G, int g,
                                  PlanScratch<NT>& sc, F&& f) {
   int len0, S0, tot0;
   const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
@@ -295,7 +336,8 @@ MLA_DEV void plan_for_each_piece(LenP seq_lens, int B, int bs, int G, int g,
     c += NT;
     lds_barrier();  // the next chunk rewrites the piece list
     const int b = c + int(threadIdx.x);
-    const int len = b < B ? seq_lens[b] : 0;
+    lens_stage(seq_lens, c);
+    const int len = b < B ? lens_get(seq_lens, b) : 0;
     const int S = carryS + block_excl_scan<NT>(units_of(len, bs), sc.red, &totN);
     totN = __builtin_amdgcn_readfirstlane(totN);
     cnt = plan_chunk<NT>(c, len, S, bs, pg, g, lo, hi, carryP, sc, &totP);
@@ -304,7 +346,7 @@ MLA_DEV void plan_for_each_piece(LenP seq_lens, int B, int bs, int G, int g,
 
 // Slot of the first piece of sequence b and its number of pieces.
 template <int NT, class LenP>
-MLA_DEV void plan_lookup(LenP seq_lens, int B, int bs, int G, int b,
+MLA_DEV void plan_lookup(LenP&& seq_lens, int B, int bs, int G, int b,
                          PlanScratch<NT>& sc, int* slot0, int* npieces) {
   int len0, S0, tot0;
   const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
@@ -318,7 +360,8 @@ MLA_DEV void plan_lookup(LenP seq_lens, int B, int bs, int G, int b,
     const int bb = c + threadIdx.x;
     int n = units_of(len0, bs), S = S0, totN = tot0;
     if (c > 0) {
-      n = bb < B ? units_of(seq_lens[bb], bs) : 0;
+      lens_stage(seq_lens, c);
+      n = bb < B ? units_of(lens_get(seq_lens, bb), bs) : 0;
       S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
     }
     const int first = n > 0 ? pg.part_of(S) : 0;
@@ -346,7 +389,7 @@ MLA_DEV void plan_lookup(LenP seq_lens, int B, int bs, int G, int b,
 // to t_slot0 / t_np (nb entries each, typically LDS).  All threads call it;
 // the tables are complete when it returns.
 template <int NT, class LenP>
-MLA_DEV void plan_slots(LenP seq_lens, int B, int bs, int G, int b_lo, int nb,
+MLA_DEV void plan_slots(LenP&& seq_lens, int B, int bs, int G, int b_lo, int nb,
                         PlanScratch<NT>& sc, int* t_slot0, int* t_np) {
   for (int i = threadIdx.x; i < nb; i += NT) {
     t_slot0[i] = 0;
@@ -362,7 +405,8 @@ MLA_DEV void plan_slots(LenP seq_lens, int B, int bs, int G, int b_lo, int nb,
       const int b = c + int(threadIdx.x);
       int n = units_of(len0, bs), S = S0, totN = tot0;
       if (c > 0) {
-        n = b < B ? units_of(seq_lens[b], bs) : 0;
+        lens_stage(seq_lens, c);
+        n = b < B ? units_of(lens_get(seq_lens, b), bs) : 0;
         S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
       }
       const int first = n > 0 ? pg.part_of(S) : 0;
