@@ -146,8 +146,9 @@ int mla_cache_append(const mla_dims *dims, const void *h, int32_t n_tokens, int3
  *             overlap q_in
  * rows = batch * n_q in mla_decode's order.  fp32 accumulation; RoPE angles in
  * fp64 with cos/sin rounded to fp32 (as in mla_cache_append); bf16 outputs
- * round to nearest even.  bf16 with d_nope a multiple of 16 and d_latent of
- * 128 runs on the matrix cores; other shapes on a VALU kernel.
+ * round to nearest even.  bf16 with d_nope = 128, d_latent = 512 and d_rope a
+ * multiple of 8 up to 64 (16-byte aligned pointers) runs on the matrix cores;
+ * other shapes on a VALU kernel.
  */
 int mla_query_absorb(const mla_dims *dims, const void *q_in, const int32_t *positions,
                      const void *w_uk, void *q_out, int32_t rows, mla_stream_t stream);
@@ -169,8 +170,10 @@ int mla_query_absorb(const mla_dims *dims, const void *q_in, const int32_t *posi
  * `num_partitions` near-equal ranges; one workgroup per (range, query token)
  * walks its range and writes, for every sequence piece it covers, a partial
  * (o = normalised latent output, lse = natural-log sum of exp of the scores)
- * into `workspace`.  mla_decode_combine merges the pieces of each sequence
- * with a log-sum-exp weighting.  num_partitions <= 0 selects the default
+ * into `workspace`, and records there, per sequence, the first slot and the
+ * number of its pieces.  mla_decode_combine merges the pieces of each sequence
+ * with a log-sum-exp weighting, reading that record (so it must follow an
+ * mla_decode on the same workspace; the stream orders the two).  num_partitions <= 0 selects the default
  * (the device's compute-unit count divided by n_q, at least 1); values above
  * MLA_MAX_PARTITIONS are rejected with MLA_ERR_INVALID_ARGUMENT (and give a
  * workspace size of 0).  Results are deterministic for a fixed num_partitions.

@@ -7,12 +7,11 @@
 //
 // One workgroup per (head, 32 rows); d_latent = 512, d_v <= 128 (multiple of
 // 32), bf16 partials and weights, fp32 accumulation.
+//  * Where each sequence's pieces sit (first slot, count) is read from the
+//    table mla_decode records beside the partials, so no plan is recomputed.
 //  * The head's W^UV_i (d_v rows of 1 KB) is copied into LDS by direct 1 KB
-//    loads (16-byte chunks XOR-swizzled by row), issued first: it streams in
-//    while the workgroup plans and merges.  The sequence lengths the plan
-//    needs are staged in LDS the same way (one wave, waited for before its
-//    share of W is issued), and the plan's barriers are LDS-only, so nothing
-//    waits for W until the MFMAs.
+//    loads (16-byte chunks XOR-swizzled by row), issued right after the table
+//    is in: it streams in while the workgroup merges.
 //  * Each wave merges 8 rows: every lane owns 8 channels; the lse values and
 //    partial rows of a chunk of 4 pieces are loaded for all 8 rows before any
 //    is used.  The merged u row is rounded to bf16 (as mla_decode_combine
@@ -43,16 +42,7 @@ struct Smem {
   alignas(128) unsigned char w[kMaxDV * kRowBytes];  // W^UV_i
   alignas(128) unsigned char u[kRows * kRowBytes];   // merged rows (bf16)
 };
-// the plan scratch, slot tables and staged lengths live in the u tile until
-// it is written
 constexpr int kMaxGroups = 8;         // row groups per workgroup (W^UV_i loaded once for all)
-constexpr int kMaxSeq = kMaxGroups * kRows + 1;
-constexpr int kLensOff = 7424;        // 256-byte aligned, past scratch and tables
-constexpr int kMaxLensLds = 4096;     // sequences whose lengths are staged in LDS
-static_assert(sizeof(PlanScratch<kNT>) + 2 * kMaxSeq * sizeof(int) <= kLensOff &&
-                  kLensOff + kMaxLensLds * 4 <= kRows * kRowBytes,
-              "plan scratch, tables and lengths must fit the u tile");
-typedef __attribute__((address_space(3))) const int32_t lds_i32;
 
 MLA_DEV uint32_t lds_addr(const unsigned char* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_u8*)p));
@@ -97,44 +87,24 @@ void combine_out_proj_kernel(CombineProjArgs a, int gpw) {
   const int ngr = (Rend - R0 + kRows - 1) / kRows;  // groups of this workgroup
 
 
-  // ---- 0. lengths (wave 0) and W^UV_i (all waves) into LDS ----
-  const bool lens_in_lds = a.batch <= kMaxLensLds && (reinterpret_cast<uintptr_t>(a.seq_lens) % 16) == 0;
-  if (lens_in_lds && wave == 0) {
-    const __amdgpu_buffer_rsrc_t rl =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.seq_lens, (short)0, a.batch * 4, 0x00020000);
-    for (int k = 0; k * 1024 < a.batch * 4; ++k)
-      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                   :
-                   : "v"(lane * 16), "s"(rl), "s"(k * 1024), "{m0}"(lds_addr(sm.u + kLensOff + k * 1024))
-                   : "memory");
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only the lengths are in flight
-  }
-  load_w_rows(sm.w, a.w_uv, h, dv, wave, lane);
-  lds_barrier();
-
-  // ---- 1. first slot and piece count of this workgroup's sequences ----
-  PlanScratch<kNT>& ps = *reinterpret_cast<PlanScratch<kNT>*>(sm.u);
-  int* t_slot0 = reinterpret_cast<int*>(sm.u + sizeof(PlanScratch<kNT>));
-  int* t_np = t_slot0 + kMaxSeq;
-  const int b_lo = R0 / a.n_q;
-  const int nb = (Rend - 1) / a.n_q - b_lo + 1;
-  if (lens_in_lds)
-    plan_slots<kNT>((lds_i32*)(uintptr_t)lds_addr(sm.u + kLensOff), a.batch, a.block_size, a.G, b_lo, nb, ps,
-                    t_slot0, t_np);
-  else
-    plan_slots<kNT>(a.seq_lens, a.batch, a.block_size, a.G, b_lo, nb, ps, t_slot0, t_np);
-  // lane l keeps the table entries of this wave's row l % 8 in group l / 8
+  // ---- 0. first slot and piece count of this wave's rows, from the table
+  // the decode recorded; lane l keeps those of row l % 8 in group l / 8 ----
   static_assert(kMaxGroups * kRowsPerWave <= kWave, "one row per lane");
   int l_slot0 = 0, l_np = 0;
   {
     const int row = R0 + (lane / kRowsPerWave) * kRows + wave * kRowsPerWave + lane % kRowsPerWave;
     if (lane / kRowsPerWave < ngr && row < Rend) {
-      const int bi = row / a.n_q - b_lo;
-      l_slot0 = t_slot0[bi];
-      l_np = t_np[bi];
+      const int2 t = *reinterpret_cast<const int2*>(a.ws_tab + 2 * (row / a.n_q));
+      l_slot0 = t.x;
+      l_np = t.y;
     }
   }
-  lds_barrier();  // the tables are read; the u tile may be overwritten
+  // consumed here, so the wait for the table comes before the W loads
+  // (waiting for it later would also wait for them)
+  asm volatile("" ::"v"(l_slot0), "v"(l_np));
+
+  // ---- 1. W^UV_i into LDS: it streams in while the rows merge ----
+  load_w_rows(sm.w, a.w_uv, h, dv, wave, lane);
 
   for (int k = 0; k < ngr; ++k) {
   const int r0 = R0 + k * kRows, nrows = min(kRows, R - r0);
@@ -299,10 +269,7 @@ struct RowSmem {
   alignas(128) unsigned char w[kMaxDV * kRowBytes];  // W^UV_i, rows swizzled as above
   alignas(16) float acc[kNT / kWave][kDC];           // per-wave unnormalised sums
   alignas(16) unsigned char u[kRowBytes];            // merged row (bf16)
-  alignas(16) int lens[kMaxRowModeRows * 8];         // staged sequence lengths (B <= R)
   float mw[kNT / kWave], sw[kNT / kWave];
-  int t_slot0[1], t_np[1];
-  PlanScratch<kNT> plan;
 };
 
 __global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -317,28 +284,12 @@ void combine_out_proj_row_kernel(CombineProjArgs a) {
   const int h = logical / R, r = logical % R;
   const int b = r / a.n_q, j = r % a.n_q;
 
-  // ---- 0. lengths (wave 0) and W^UV_i (all waves) into LDS ----
-  const bool lens_in_lds = (reinterpret_cast<uintptr_t>(a.seq_lens) % 16) == 0;
-  if (lens_in_lds && wave == 0) {
-    const __amdgpu_buffer_rsrc_t rl =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.seq_lens, (short)0, a.batch * 4, 0x00020000);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(lane * 16), "s"(rl), "{m0}"(lds_addr(reinterpret_cast<unsigned char*>(sm.lens)))
-                 : "memory");
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  // ---- 0. the row's first slot and piece count (as the decode recorded
+  // them), then W^UV_i into LDS ----
+  const int slot0 = __builtin_amdgcn_readfirstlane(a.ws_tab[2 * b]);
+  const int np = __builtin_amdgcn_readfirstlane(a.ws_tab[2 * b + 1]);
+  asm volatile("" ::"s"(slot0), "s"(np));  // waited for before the W loads are issued
   load_w_rows(sm.w, a.w_uv, h, dv, wave, lane);
-  lds_barrier();
-
-  // ---- 1. the row's first slot and piece count ----
-  if (lens_in_lds)
-    plan_slots<kNT>((lds_i32*)(uintptr_t)lds_addr(reinterpret_cast<unsigned char*>(sm.lens)), a.batch,
-                    a.block_size, a.G, b, 1, sm.plan, sm.t_slot0, sm.t_np);
-  else
-    plan_slots<kNT>(a.seq_lens, a.batch, a.block_size, a.G, b, 1, sm.plan, sm.t_slot0, sm.t_np);
-  const int slot0 = __builtin_amdgcn_readfirstlane(sm.t_slot0[0]);
-  const int np = __builtin_amdgcn_readfirstlane(sm.t_np[0]);
 
   // ---- 2. this wave's pieces: w, w + 4, ... (lane = 8 channels) ----
   const size_t pstride = size_t(a.n_q) * H;

@@ -51,6 +51,8 @@ __global__ __launch_bounds__(kGenNT) void decode_generic_kernel(DecodeArgs a) {
   const int g = blockIdx.x / (H * a.n_q);
   const int tid = threadIdx.x;
 
+  // the (j = 0, head 0) workgroup of each partition records the slot table
+  int32_t* const tab = (i == 0 && j == 0) ? a.ws_tab : nullptr;
   plan_for_each_piece<kGenNT>(a.seq_lens, a.batch, bs, a.G, g, plan,
                               [&](int b, int ulo, int uhi, int slot, int L) {
     const int nvis = L - a.n_q + j + 1;  // positions 0 .. L - n_q + j
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kGenNT) void decode_generic_kernel(DecodeArgs a) {
       }
     }
     if (tid == 0) a.ws_lse[obase] = l > 0.f ? m + logf(l) : -INFINITY;
-  });
+  }, tab);
 }
 
 template <int CDT, int ADT>
@@ -181,12 +183,10 @@ struct Raw8 {
 // NV = 8-channel vectors per lane (d_latent <= 512 * NV)
 template <int ADT, int NV>
 __global__ __launch_bounds__(kCombNT) void combine_kernel(CombineArgs a) {
-  __shared__ PlanScratch<kCombNT> plan;
   const int bj = blockIdx.x;
   const int b = bj / a.n_q, j = bj % a.n_q;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  int slot0, np;
-  plan_lookup<kCombNT>(a.seq_lens, a.batch, a.block_size, a.G, b, plan, &slot0, &np);
+  const int slot0 = a.ws_tab[2 * b], np = a.ws_tab[2 * b + 1];
   const int H = a.H, dc = a.d_latent, nvec = dc / 8;
   const int h0 = blockIdx.y * kCombHeads + w * kCHW;
   float M[kCHW], wsum[kCHW], acc[kCHW][NV][8];
@@ -279,12 +279,10 @@ bool combine_vector_ok(const CombineArgs& a) { return a.d_latent % 8 == 0 && a.d
 // Scalar fallback (any d_latent): one thread per channel.
 template <int ADT>
 __global__ __launch_bounds__(kCombNT) void combine_scalar_kernel(CombineArgs a) {
-  __shared__ PlanScratch<kCombNT> plan;
   const int bj = blockIdx.x;
   const int b = bj / a.n_q, j = bj % a.n_q;
   const int h = blockIdx.y;
-  int slot0, np;
-  plan_lookup<kCombNT>(a.seq_lens, a.batch, a.block_size, a.G, b, plan, &slot0, &np);
+  const int slot0 = a.ws_tab[2 * b], np = a.ws_tab[2 * b + 1];
   const int H = a.H, dc = a.d_latent;
   float M = -INFINITY;
   for (int s = 0; s < np; ++s) M = fmaxf(M, a.ws_lse[(size_t(slot0 + s) * a.n_q + j) * H + h]);

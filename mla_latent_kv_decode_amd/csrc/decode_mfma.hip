@@ -336,6 +336,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   lds_barrier();
   bool q_pre = true;  // the prefetched Q may still serve the first piece
 
+  int32_t* const tab = j == 0 ? a.ws_tab : nullptr;  // query 0's workgroups record the slot table
   plan_for_each_piece<kNT>(lens, a.batch, kBS, a.G, part, sm.plan,
                            [&](int b_, int ulo_, int uhi_, int slot_, int L_) {
     // piece bounds come from LDS: tell the compiler they are wave-uniform
@@ -600,7 +601,7 @@ void decode_mfma_kernel(DecodeArgs a) {
       __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + r * kStageRow + elane * 16),
                                   orow + r * (kDC / 8));
     step_barrier();  // every wave is done with the stage before a next piece loads into it
-  });
+  }, tab);
   wait_vm<0>();  // a prefetched Q no piece used must land before the workgroup's LDS is released
 }
 

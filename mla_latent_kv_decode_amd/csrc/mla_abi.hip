@@ -65,8 +65,11 @@ int default_partitions(int n_q) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Decode workspace: partials o [slots][n_q][H][d_latent] (act dtype), their
+// lse [slots][n_q][H] fp32, and per sequence (first slot, piece count)
+// int32 [B][2], which mla_decode records for the combine.
 struct WsLayout {
-  size_t o_bytes, lse_off, total;
+  size_t o_bytes, lse_off, tab_off, total;
 };
 
 WsLayout ws_layout(const mla_dims* d, int batch, int n_q, int G) {
@@ -74,7 +77,8 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q, int G) {
   WsLayout w;
   w.o_bytes = slots * size_t(n_q) * d->num_heads * d->d_latent * elem_bytes(d->act_dtype);
   w.lse_off = align_up(w.o_bytes, 256);
-  w.total = align_up(w.lse_off + slots * size_t(n_q) * d->num_heads * sizeof(float), 256);
+  w.tab_off = align_up(w.lse_off + slots * size_t(n_q) * d->num_heads * sizeof(float), 256);
+  w.total = align_up(w.tab_off + size_t(batch) * 2 * sizeof(int32_t), 256);
   return w;
 }
 
@@ -209,6 +213,7 @@ int mla_decode(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, con
   a.seq_lens = seq_lens;
   a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.lse_off);
+  a.ws_tab = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + w.tab_off);
   a.batch = batch;
   a.n_q = n_q;
   a.H = d->num_heads;
@@ -252,6 +257,7 @@ int mla_decode_combine(const mla_dims* d, const void* workspace, size_t workspac
   mla::CombineArgs a;
   a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.lse_off);
+  a.ws_tab = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + w.tab_off);
   a.seq_lens = seq_lens;
   a.u = u_out;
   a.lse_out = lse_out;
@@ -350,6 +356,7 @@ int mla_decode_combine_out_proj(const mla_dims* d, const void* workspace, size_t
   mla::CombineProjArgs a;
   a.ws_o = workspace;
   a.ws_lse = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + w.lse_off);
+  a.ws_tab = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + w.tab_off);
   a.seq_lens = seq_lens;
   a.w_uv = w_uv;
   a.out = out;

@@ -286,10 +286,14 @@ MLA_DEV int plan_total_units(LenP&& seq_lens, int B, int bs, PlanScratch<NT>& sc
 // One chunk of sequences [c, c + NT): writes the pieces of partition g that
 // fall in it to sc (in sequence order) and returns their number.  len/S are
 // this thread's sequence length and global unit prefix; totP receives the
-// chunk's piece total.
+// chunk's piece total.  With tab non-null, the partition that owns a
+// sequence's first unit (for an empty sequence: the one that owns unit S_b,
+// or the last) also records the sequence's first slot and piece count in
+// tab[2b], tab[2b + 1] -- exactly one partition per sequence, so the combine
+// kernels need not plan.
 template <int NT>
 MLA_DEV int plan_chunk(int c, int len, int S, int bs, const PartGrid& pg, int g, int64_t lo,
-                       int64_t hi, int carryP, PlanScratch<NT>& sc, int* totP) {
+                       int64_t hi, int carryP, PlanScratch<NT>& sc, int* totP, int B, int32_t* tab) {
   const int n = units_of(len, bs);
   const int first = n > 0 ? pg.part_of(S) : 0;
   const int pieces = n > 0 ? pg.part_of(int64_t(S) + n - 1) - first + 1 : 0;
@@ -303,6 +307,14 @@ MLA_DEV int plan_chunk(int c, int len, int S, int bs, const PartGrid& pg, int g,
     sc.slot[r.y] = carryP + r.x + (g - first);
     sc.len[r.y] = len;
   }
+  const int b = c + int(threadIdx.x);
+  if (tab && b < B) {
+    const int owner = n > 0 ? first : min(pg.part_of(S), pg.G - 1);
+    if (owner == g) {
+      tab[2 * b] = carryP + r.x;
+      tab[2 * b + 1] = pieces;
+    }
+  }
   lds_barrier();
   return cnt;
 }
@@ -314,23 +326,29 @@ MLA_DEV int plan_chunk(int c, int len, int S, int bs, const PartGrid& pg, int g,
 // before the loop), so f gets the whole register file.
 template <int NT, class LenP, class F>
 MLA_DEV void plan_for_each_piece(LenP&& seq_lens, int B, int bs, int G, int g,
-                                 PlanScratch<NT>& sc, F&& f) {
+                                 PlanScratch<NT>& sc, F&& f, int32_t* tab = nullptr) {
   int len0, S0, tot0;
   const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
-  if (T == 0) return;
+  if (T == 0) {  // nothing to attend: every sequence has no pieces
+    if (tab && g == 0)
+      for (int b = threadIdx.x; b < B; b += NT) tab[2 * b] = tab[2 * b + 1] = 0;
+    return;
+  }
   G = min(G, T);
   if (g >= G) return;
   const PartGrid pg(T, G);
   const int64_t lo = uniform64(pg.lo(g)), hi = uniform64(pg.lo(g + 1));
   if (lo >= hi) return;
   int totP;
-  int cnt = plan_chunk<NT>(0, len0, S0, bs, pg, g, lo, hi, 0, sc, &totP);
+  int cnt = plan_chunk<NT>(0, len0, S0, bs, pg, g, lo, hi, 0, sc, &totP, B, tab);
   int c = 0, carryS = 0, carryP = 0, totN = tot0;
   for (;;) {
     cnt = __builtin_amdgcn_readfirstlane(cnt);
     for (int k = 0; k < cnt; ++k)
       f(sc.b[k], sc.ulo[k], sc.uhi[k], sc.slot[k], sc.len[k]);
-    if (c + NT >= B || carryS + totN >= hi) return;
+    // (the last partition goes on to the end: trailing empty sequences are
+    // recorded by it)
+    if (c + NT >= B || (carryS + totN >= hi && !(tab && g == G - 1))) return;
     carryS = __builtin_amdgcn_readfirstlane(carryS + totN);
     carryP = __builtin_amdgcn_readfirstlane(carryP + totP);
     c += NT;
@@ -340,96 +358,12 @@ MLA_DEV void plan_for_each_piece(LenP&& seq_lens, int B, int bs, int G, int g,
     const int len = b < B ? lens_get(seq_lens, b) : 0;
     const int S = carryS + block_excl_scan<NT>(units_of(len, bs), sc.red, &totN);
     totN = __builtin_amdgcn_readfirstlane(totN);
-    cnt = plan_chunk<NT>(c, len, S, bs, pg, g, lo, hi, carryP, sc, &totP);
+    cnt = plan_chunk<NT>(c, len, S, bs, pg, g, lo, hi, carryP, sc, &totP, B, tab);
   }
 }
 
-// Slot of the first piece of sequence b and its number of pieces.
-template <int NT, class LenP>
-MLA_DEV void plan_lookup(LenP&& seq_lens, int B, int bs, int G, int b,
-                         PlanScratch<NT>& sc, int* slot0, int* npieces) {
-  int len0, S0, tot0;
-  const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);
-  *slot0 = 0;
-  *npieces = 0;
-  if (T == 0) return;
-  G = min(G, T);
-  const PartGrid pg(T, G);
-  int carryS = 0, carryP = 0;
-  for (int c = 0; c <= b; c += NT) {
-    const int bb = c + threadIdx.x;
-    int n = units_of(len0, bs), S = S0, totN = tot0;
-    if (c > 0) {
-      lens_stage(seq_lens, c);
-      n = bb < B ? units_of(lens_get(seq_lens, bb), bs) : 0;
-      S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
-    }
-    const int first = n > 0 ? pg.part_of(S) : 0;
-    const int pieces = n > 0 ? pg.part_of(int64_t(S) + n - 1) - first + 1 : 0;
-    int totP;
-    const int P = carryP + block_excl_scan<NT>(pieces, sc.red, &totP);
-    if (bb == b) {
-      sc.b[0] = P;
-      sc.ulo[0] = pieces;
-    }
-    lds_barrier();
-    if (b < c + NT) {
-      *slot0 = sc.b[0];
-      *npieces = sc.ulo[0];
-      lds_barrier();
-      return;
-    }
-    lds_barrier();
-    carryS += totN;
-    carryP += totP;
-  }
-}
-
-// First slot and piece count of every sequence in [b_lo, b_lo + nb), written
-// to t_slot0 / t_np (nb entries each, typically LDS).  All threads call it;
-// the tables are complete when it returns.
-template <int NT, class LenP>
-MLA_DEV void plan_slots(LenP&& seq_lens, int B, int bs, int G, int b_lo, int nb,
-                        PlanScratch<NT>& sc, int* t_slot0, int* t_np) {
-  for (int i = threadIdx.x; i < nb; i += NT) {
-    t_slot0[i] = 0;
-    t_np[i] = 0;
-  }
-  int len0, S0, tot0;
-  const int T = plan_total_units<NT>(seq_lens, B, bs, sc, &len0, &S0, &tot0);  // barriers order the zeroing
-  if (T > 0) {
-    G = min(G, T);
-    const PartGrid pg(T, G);
-    int carryS = 0, carryP = 0;
-    for (int c = 0; c < B && c < b_lo + nb; c += NT) {
-      const int b = c + int(threadIdx.x);
-      int n = units_of(len0, bs), S = S0, totN = tot0;
-      if (c > 0) {
-        lens_stage(seq_lens, c);
-        n = b < B ? units_of(lens_get(seq_lens, b), bs) : 0;
-        S = carryS + block_excl_scan<NT>(n, sc.red, &totN);
-      }
-      const int first = n > 0 ? pg.part_of(S) : 0;
-      const int pieces = n > 0 ? pg.part_of(int64_t(S) + n - 1) - first + 1 : 0;
-      int totP;
-      const int P = carryP + block_excl_scan<NT>(pieces, sc.red, &totP);
-      if (b >= b_lo && b < b_lo + nb && b < B) {
-        t_slot0[b - b_lo] = P;
-        t_np[b - b_lo] = pieces;
-      }
-      carryS += totN;
-      carryP += totP;
-    }
-  }
-  lds_barrier();
-}
-
-// Workspace layout: [o: n_slots][n_q][H][d_latent] in the activation dtype |
-// [lse: n_slots][n_q][H] fp32.
-struct Workspace {
-  float* o;
-  float* lse;
-};
+// Partial slots a decode over B sequences and G partitions can fill: each
+// partition starts at most one piece that is not some sequence's first.
 static inline __host__ __device__ size_t ws_slots(int B, int G) { return size_t(B) + size_t(G); }
 
 }  // namespace mla

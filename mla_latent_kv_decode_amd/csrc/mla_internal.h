@@ -13,6 +13,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   void* ws_o;              // [slots][n_q][H][d_latent] act dtype (normalised partials)
   float* ws_lse;           // [slots][n_q][H]
+  int32_t* ws_tab;         // [B][2]: first slot, piece count (written by the plan)
   int batch, n_q, H, D, d_latent, block_size, max_blocks, G;
   int cache_dtype, act_dtype;
   float scale;
@@ -21,6 +22,7 @@ struct DecodeArgs {
 struct CombineArgs {
   const void* ws_o;        // act dtype
   const float* ws_lse;
+  const int32_t* ws_tab;   // [B][2] as recorded by the decode
   const int32_t* seq_lens;
   void* u;                 // [B][n_q][H][d_latent] act dtype
   float* lse_out;          // [B][n_q][H] or null
@@ -32,6 +34,7 @@ struct CombineArgs {
 struct CombineProjArgs {
   const void* ws_o;        // bf16 partials
   const float* ws_lse;
+  const int32_t* ws_tab;   // [B][2] as recorded by the decode
   const int32_t* seq_lens;
   const void* w_uv;        // [H][d_v][d_latent]
   void* out;               // [B * n_q][H][d_v]

@@ -85,7 +85,9 @@ def test_workspace_size_closed_form(L):
     slots = B + G
     o = slots * n_q * H * dc * 2          # partials are stored in the bf16 activation dtype
     lse = slots * n_q * H * 4
-    want = (((o + 255) // 256 * 256 + lse) + 255) // 256 * 256
+    up = lambda x: (x + 255) // 256 * 256
+    tab = B * 2 * 4                       # first slot and piece count per sequence
+    want = up(up(up(o) + lse) + tab)
     assert L.mla_decode_workspace_size(d, B, n_q, G) == want
     assert L.mla_decode_workspace_size(d, B, 0, G) == 0
 
