@@ -154,6 +154,29 @@ int mla_query_absorb(const mla_dims *dims, const void *q_in, const int32_t *posi
                      const void *w_uk, void *q_out, int32_t rows, mla_stream_t stream);
 
 /*
+ * mla_linear -- y = x W^T, a bias-free linear layer with fp32 accumulation:
+ * the query projections of the [MLA-93] decoding section (c^Q = W^DQ h, then
+ * q^C = W^UQ c^Q and q^R = W^QR c^Q; placing the rows of W^UQ and W^QR head
+ * by head, [W^UQ_i ; W^QR_i], gives mla_query_absorb's q_in in one call) and
+ * its final output projection W^O.
+ *   x  [rows][k] act_dtype
+ *   w  [n][k]    act_dtype (a torch Linear weight)
+ *   y  [rows][n] act_dtype; must not overlap x or w
+ *   workspace: device scratch of mla_linear_workspace_size(dims, rows, n, k)
+ *              bytes, 16-byte aligned (NULL when that size is 0)
+ * bf16 outputs round to nearest even.  bf16 with k a multiple of 512 and n of
+ * 32 (16-byte aligned x, w, y) runs on the matrix cores (the k range may be
+ * split, the fp32 partials kept in the workspace and summed in a fixed order:
+ * results are deterministic); other shapes on a VALU kernel.
+ * Errors: MLA_ERR_INVALID_ARGUMENT (rows < 0, k < 1, n < 1, NULL, misaligned,
+ * overlap), MLA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t mla_linear_workspace_size(const mla_dims *dims, int32_t rows, int32_t n, int32_t k);
+
+int mla_linear(const mla_dims *dims, const void *x, int32_t rows, int32_t k, const void *w, int32_t n,
+               void *y, void *workspace, size_t workspace_bytes, mla_stream_t stream);
+
+/*
  * Split-KV decode (mla_decode + mla_decode_combine).
  *
  * q [batch][n_q][num_heads][d_latent + d_rope] act_dtype: packed absorbed

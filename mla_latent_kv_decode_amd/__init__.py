@@ -8,5 +8,6 @@ from ._lib import (  # noqa: F401
     BF16, EXPORTS, FLAG_GENERIC_DECODE, FP32, FP8_E4M3, LIB_PATH, MlaError, lib, make_dims,
     mla_abi_version, mla_cache_append, mla_cache_append_workspace_size, mla_decode,
     mla_decode_combine, mla_decode_combine_out_proj, mla_decode_workspace_size,
-    mla_device_cu_count, mla_dims, mla_out_proj, mla_query_absorb,
+    mla_device_cu_count, mla_dims, mla_linear, mla_linear_workspace_size, mla_out_proj,
+    mla_query_absorb,
 )

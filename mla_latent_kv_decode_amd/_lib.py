@@ -27,7 +27,8 @@ ERR_HIP = -4
 EXPORTS = ("mla_abi_version", "mla_last_error", "mla_device_cu_count",
            "mla_cache_append_workspace_size", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_combine", "mla_out_proj",
-           "mla_decode_combine_out_proj", "mla_query_absorb")
+           "mla_decode_combine_out_proj", "mla_query_absorb", "mla_linear_workspace_size",
+           "mla_linear")
 
 
 class MlaError(RuntimeError):
@@ -87,8 +88,11 @@ def lib():
         L.mla_decode_combine_out_proj.argtypes = [D, _P, ctypes.c_size_t, _I, _I, _P, _I, _P, _P,
                                                   _P, _P, _P]
         L.mla_query_absorb.argtypes = [D, _P, _P, _P, _P, _I, _P]
+        L.mla_linear_workspace_size.argtypes = [D, _I, _I, _I]
+        L.mla_linear_workspace_size.restype = ctypes.c_size_t
+        L.mla_linear.argtypes = [D, _P, _I, _I, _P, _I, _P, _P, ctypes.c_size_t, _P]
         for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj",
-                  "mla_decode_combine_out_proj", "mla_query_absorb"):
+                  "mla_decode_combine_out_proj", "mla_query_absorb", "mla_linear"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -181,3 +185,18 @@ def mla_query_absorb(dims, q_in, positions, w_uk, q_out, stream=None):
     rows = q_in.numel() // (dims.num_heads * (dims.d_nope + dims.d_rope))
     _check(lib().mla_query_absorb(ctypes.byref(dims), _ptr(q_in), _ptr(positions), _ptr(w_uk),
                                   _ptr(q_out), rows, _stream(stream)))
+
+
+def mla_linear_workspace_size(dims, rows: int, n: int, k: int) -> int:
+    return lib().mla_linear_workspace_size(ctypes.byref(dims), rows, n, k)
+
+
+def mla_linear(dims, x, w, y, workspace=None, stream=None):
+    """y = x W^T: x [rows, k] (any leading shape whose product is rows); w [n, k];
+    y [rows, n]; workspace a device tensor of mla_linear_workspace_size bytes
+    (or None if that is 0)."""
+    k = x.shape[-1]
+    rows = x.numel() // k
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_linear(ctypes.byref(dims), _ptr(x), rows, k, _ptr(w), w.shape[0], _ptr(y),
+                            _ptr(workspace), wsb, _stream(stream)))

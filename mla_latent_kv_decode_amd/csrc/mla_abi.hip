@@ -82,6 +82,23 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q, int G) {
   return w;
 }
 
+// Shared checks of mla_linear and its workspace query; fills a.
+int linear_args(const mla_dims* d, const void* x, int32_t rows, int32_t k, const void* w, int32_t n,
+                void* y, mla::LinearArgs* a) {
+  if (int e = check_dims(d, false)) return e;
+  if (rows < 0 || k < 1 || n < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "rows=%d k=%d n=%d", rows, k, n);
+  a->x = x;
+  a->w = w;
+  a->y = y;
+  a->rows = rows;
+  a->n = n;
+  a->k = k;
+  a->act_dtype = d->act_dtype;
+  return MLA_OK;
+}
+bool linear_use_mfma(const mla_dims* d, const mla::LinearArgs& a) {
+  return !(d->flags & MLA_FLAG_GENERIC_DECODE) && a.rows > 0 && mla::linear_mfma_supported(a);
+}
 }  // namespace
 
 extern "C" {
@@ -304,6 +321,44 @@ int mla_query_absorb(const mla_dims* d, const void* q_in, const int32_t* positio
   hipError_t e = mfma ? mla::launch_query_absorb_mfma(a, static_cast<hipStream_t>(stream))
                       : mla::launch_query_absorb_generic(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "query_absorb launch");
+  return ok();
+}
+
+size_t mla_linear_workspace_size(const mla_dims* d, int32_t rows, int32_t n, int32_t k) {
+  mla::LinearArgs a;
+  // The kernel choice also depends on the pointers' alignment, unknown here:
+  // the size is that of the matrix-core form whenever dtype and shapes allow it
+  // (16-byte aligned stand-in pointers).
+  if (linear_args(d, reinterpret_cast<const void*>(uintptr_t(256)), rows, k,
+                  reinterpret_cast<const void*>(uintptr_t(256)), n, reinterpret_cast<void*>(uintptr_t(256)), &a))
+    return 0;
+  return linear_use_mfma(d, a) ? mla::linear_mfma_workspace(a) : 0;
+}
+
+int mla_linear(const mla_dims* d, const void* x, int32_t rows, int32_t k, const void* w, int32_t n, void* y,
+               void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+  mla::LinearArgs a;
+  if (int e = linear_args(d, x, rows, k, w, n, y, &a)) return e;
+  if (rows == 0) return ok();
+  if (!x || !w || !y) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t ae = elem_bytes(d->act_dtype);
+  if (!aligned(x, ae) || !aligned(w, ae) || !aligned(y, ae) || (workspace && !aligned(workspace, 16)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), w0 = reinterpret_cast<uintptr_t>(w),
+                  y0 = reinterpret_cast<uintptr_t>(y);
+  const size_t xb = size_t(rows) * k * ae, wbytes = size_t(n) * k * ae, yb = size_t(rows) * n * ae;
+  if ((y0 < x0 + xb && x0 < y0 + yb) || (y0 < w0 + wbytes && w0 < y0 + yb))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "y overlaps x or w");
+  hipError_t e;
+  if (linear_use_mfma(d, a)) {
+    const size_t need = mla::linear_mfma_workspace(a);
+    if (workspace_bytes < need || (need && !workspace))
+      return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    e = mla::launch_linear_mfma(a, workspace, static_cast<hipStream_t>(stream));
+  } else {
+    e = mla::launch_linear_generic(a, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
   return ok();
 }
 

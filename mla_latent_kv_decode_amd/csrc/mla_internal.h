@@ -71,6 +71,20 @@ bool query_absorb_mfma_supported(const QueryArgs& a);
 hipError_t launch_query_absorb_mfma(const QueryArgs& a, hipStream_t st);
 hipError_t launch_query_absorb_generic(const QueryArgs& a, hipStream_t st);
 
+// y = x W^T
+struct LinearArgs {
+  const void* x;           // [rows][k]
+  const void* w;           // [n][k]
+  void* y;                 // [rows][n]
+  int rows, n, k;
+  int act_dtype;
+};
+
+bool linear_mfma_supported(const LinearArgs& a);
+size_t linear_mfma_workspace(const LinearArgs& a);
+hipError_t launch_linear_mfma(const LinearArgs& a, void* ws, hipStream_t st);
+hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t st);
+
 struct OutProjArgs {
   const void* u;           // [rows][H][d_latent]
   const void* w;           // [H][d_v][d_latent]

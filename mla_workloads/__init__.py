@@ -38,6 +38,7 @@ class Dims:
     d_nope: int
     d_v: int
     d_model: int
+    d_q: int = 0                # query compression width (W^DQ rows); 0: a single W^Q
     block_size: int = BLOCK
     rope_base: float = 10000.0
 
@@ -48,7 +49,7 @@ class Dims:
 
 
 TINY = Dims(num_heads=4, d_latent=32, d_rope=8, d_nope=16, d_v=16, d_model=64)
-V3 = Dims(num_heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128, d_model=7168)
+V3 = Dims(num_heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128, d_model=7168, d_q=1536)
 
 
 @dataclasses.dataclass(frozen=True)

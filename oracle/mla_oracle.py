@@ -458,6 +458,35 @@ def query_from_hidden(h_q, w_q, w_uk, pos, n_heads: int, d_nope: int, d_rope: in
 
 
 # --------------------------------------------------------------------------
+# the decoding section's dense layers: the low-rank query path and W^O
+# ([MLA-93] decoding section: its W_DQ, W_UQ, W_QR and W_O Linears)
+# --------------------------------------------------------------------------
+
+def linear(x, w) -> np.ndarray:
+    """A bias-free linear layer y = x W^T, with W stored [n, k] as a torch
+    Linear keeps it (the module's every projection is bias-free)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def query_lowrank(h, w_dq, w_uq, w_qr, n_heads: int, d_nope: int, d_rope: int):
+    """Step 2 of the decoding procedure: the compressed query c^Q = W^DQ h,
+    then q^C = W^UQ c^Q and q^R = W^QR c^Q, each viewed head-major as
+    [.., H, d_nope] and [.., H, d_R] (q^R not yet rotated)."""
+    c_q = linear(h, w_dq)
+    q_c = linear(c_q, w_uq)
+    q_r = linear(c_q, w_qr)
+    return (q_c.reshape(q_c.shape[:-1] + (n_heads, d_nope)),
+            q_r.reshape(q_r.shape[:-1] + (n_heads, d_rope)))
+
+
+def output_projection(v, w_o) -> np.ndarray:
+    """The module's last step: the per-head outputs v [.., H, d_v] are laid
+    end to end (head-major, [.., H * d_v]) and projected by W^O [d, H d_v]."""
+    v = np.asarray(v, dtype=np.float64)
+    return linear(v.reshape(v.shape[:-2] + (v.shape[-2] * v.shape[-1],)), w_o)
+
+
+# --------------------------------------------------------------------------
 # footprint arithmetic ([MLA-93] bottleneck and cached-scalar sections;
 # [V3-ARCH] 1)
 # --------------------------------------------------------------------------

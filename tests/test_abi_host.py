@@ -152,3 +152,34 @@ def test_query_absorb_validates(L):
     assert "overlap" in lib.mla_last_error().decode()
     no_nope = _dims(L, d_nope=0, softmax_scale=0.1)
     assert call(ctypes.byref(no_nope)) == L.ERR_INVALID_ARGUMENT
+
+
+def test_linear_validates_and_sizes_its_workspace(L):
+    lib = L.lib()
+    d = _dims(L)
+    # the weight-streaming shapes of the decode step's neighbours: W^DQ and W^O
+    # split k (fp32 partials in the workspace), the wide W^UQ|W^QR does not
+    assert L.mla_linear_workspace_size(d, 64, 1536, 7168) == 7 * 64 * 1536 * 4
+    assert L.mla_linear_workspace_size(d, 64, 7168, 16384) == 4 * 64 * 7168 * 4
+    assert L.mla_linear_workspace_size(d, 64, 128 * 192, 1536) == 0
+    assert L.mla_linear_workspace_size(d, 64, 100, 7168) == 0          # n % 32: VALU form
+    assert L.mla_linear_workspace_size(d, 64, 128, 7000) == 0          # k % 512: VALU form
+    assert L.mla_linear_workspace_size(_dims(L, act_dtype=L.FP32), 64, 1536, 7168) == 0
+    assert L.mla_linear_workspace_size(d, -1, 64, 512) == 0
+    X, W, Y = FAKE, FAKE * 64, FAKE * 128
+    ws = L.mla_linear_workspace_size(d, 64, 1536, 7168)
+    call = lambda dims, x=X, rows=64, k=7168, w=W, n=1536, y=Y, wsp=FAKE * 256, wsb=ws: \
+        lib.mla_linear(dims, x, rows, k, w, n, y, wsp, wsb, None)
+    assert call(None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), x=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), w=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), y=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), rows=-1) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), k=0) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), n=0) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), rows=0) == L.OK
+    assert call(ctypes.byref(d), x=X + 1) == L.ERR_INVALID_ARGUMENT       # misaligned bf16
+    assert call(ctypes.byref(d), y=X + 64) == L.ERR_INVALID_ARGUMENT      # y overlaps x
+    assert "overlap" in lib.mla_last_error().decode()
+    assert call(ctypes.byref(d), wsb=ws - 1) == L.ERR_WORKSPACE_TOO_SMALL
+    assert call(ctypes.byref(d), wsp=None) == L.ERR_WORKSPACE_TOO_SMALL

@@ -55,10 +55,11 @@ def test_tiny_end_to_end_fp32():
     o_ref = O.out_proj(u_ref, w_uv)
     # GPU: contiguous cache = identity page table over 2 blocks of 64
     dims = dims_of(cfg)
-    # query: the projection W^Q h is the caller's (torch); absorption + q-RoPE on the GPU
-    q_full = (_t(h[64:65], torch.float32) @ _t(w_q, torch.float32).T).view(1, H, d.d_nope + d.d_rope)
+    # query: projection W^Q h, absorption and q-RoPE, all on the GPU
+    q_full = torch.empty(1, H, d.d_nope + d.d_rope, device="cuda")
+    M.mla_linear(dims, _t(h[64:65], torch.float32), _t(w_q, torch.float32), q_full)
     q_gpu = torch.empty(1, H, d.row, device="cuda")
-    M.mla_query_absorb(dims, q_full.contiguous(), torch.tensor([64], dtype=torch.int32, device="cuda"),
+    M.mla_query_absorb(dims, q_full, torch.tensor([64], dtype=torch.int32, device="cuda"),
                        _t(w_uk, torch.float32), q_gpu)
     cache = torch.full((2, 64, d.row), float("nan"), device="cuda")
     table = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
@@ -83,6 +84,125 @@ def test_tiny_end_to_end_fp32():
     assert rel_l2(o.cpu().numpy(), o_ref) <= 1e-5
     assert max_abs(o.cpu().numpy(), o_ref) <= 2e-2
     assert torch.isnan(cache.view(-1, d.row)[65:]).all(), "slots past the sequence were written"
+
+
+# --------------------------------------------------------------------------
+# dense layers (mla_linear): the low-rank query path and W^O
+# --------------------------------------------------------------------------
+LINEAR_SHAPES = [   # (rows, n, k)
+    (64, 1536, 7168),       # W^DQ at B = 64: k split in 7 ranges, partials summed in order
+    (64, 128 * 192, 1536),  # [W^UQ_i ; W^QR_i] head by head: one k range, direct bf16 store
+    (64, 7168, 16384),      # W^O: k split in 4, two column blocks per workgroup
+    (1, 32, 512),           # one row, one stage, one workgroup
+    (33, 96, 1536),         # two row blocks, the second ragged; three stages
+    (100, 64, 8192),        # two row tiles, the second ragged; k split in 4
+    (7, 64, 1000),          # k % 512 != 0: the VALU form in bf16
+]
+
+
+def _linear(M, dims, x, w, y):
+    rows, k = x.shape[0], x.shape[-1]
+    nws = M.mla_linear_workspace_size(dims, rows, w.shape[0], k)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    M.mla_linear(dims, x, w, y, ws)
+
+
+@pytest.mark.parametrize("shape", LINEAR_SHAPES)
+def test_linear_bf16_matches_oracle(shape):
+    import mla_latent_kv_decode_amd as M
+    rows, n, k = shape
+    dims = dims_of(W.CONFIGS["v3"])
+    x = W.normal((rows, k), 200 + rows, device="cuda", dtype=torch.bfloat16)
+    w = W.weight(n, k, 300 + n, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((rows, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    _linear(M, dims, x, w, y)
+    torch.cuda.synchronize()
+    got, ref = to_f64(y), O.linear(to_f64(x), to_f64(w))
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2
+    # fp32 accumulation, one round-to-nearest-even bf16 store
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4)
+
+
+def test_linear_generic_fp32_tight():
+    import mla_latent_kv_decode_amd as M
+    dims = dims_of(W.CONFIGS["tiny"])
+    x = W.normal((7, 300), 210, device="cuda")
+    w = W.weight(96, 300, 211, device="cuda")
+    y = torch.empty(7, 96, device="cuda")
+    _linear(M, dims, x, w, y)
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy().astype(np.float64), O.linear(to_f64(x), to_f64(w))) <= 1e-6
+
+
+def test_linear_mfma_agrees_with_generic_and_is_deterministic():
+    import mla_latent_kv_decode_amd as M
+    x = W.normal((40, 4096), 220, device="cuda", dtype=torch.bfloat16)
+    w = W.weight(320, 4096, 221, dtype=torch.bfloat16, device="cuda")
+    outs = []
+    for flags in (0, 0, M.FLAG_GENERIC_DECODE):
+        y = torch.empty(40, 320, dtype=torch.bfloat16, device="cuda")  # k split in 4
+        _linear(M, dims_of(W.CONFIGS["v3"], flags), x, w, y)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "the split-k sum order is fixed"
+    # same products summed in another order: at most a bf16 rounding apart
+    assert rel_l2(to_f64(outs[0]), to_f64(outs[2])) <= 2e-3
+
+
+def test_query_path_low_rank_v3():
+    """The decoding section's step 2 and 3 at B = 64 on the GPU: c^Q = W^DQ h,
+    [q^C ; q^R] per head from the head-by-head stacked [W^UQ_i ; W^QR_i] (one
+    call), then absorption and q-RoPE."""
+    import mla_latent_kv_decode_amd as M
+    d, rows = W.V3, 64
+    H, dn, dr, dq = d.num_heads, d.d_nope, d.d_rope, d.d_q
+    dims = dims_of(W.CONFIGS["v3"])
+    bf = torch.bfloat16
+    h = W.normal((rows, d.d_model), 230, device="cuda", dtype=bf)
+    w_dq = W.weight(dq, d.d_model, 231, dtype=bf, device="cuda")
+    w_uq = W.weight(H * dn, dq, 232, dtype=bf, device="cuda")
+    w_qr = W.weight(H * dr, dq, 233, dtype=bf, device="cuda")
+    w_uk = W.normal((H, dn, d.d_latent), 234, std=1 / math.sqrt(d.d_latent), device="cuda", dtype=bf)
+    pos = np.random.default_rng(235).integers(0, 131072, size=rows).astype(np.int32)
+    # weight layout, once per model: rows of head i are [W^UQ_i ; W^QR_i]
+    w_uqr = torch.cat([w_uq.view(H, dn, dq), w_qr.view(H, dr, dq)], 1).reshape(H * (dn + dr), dq).contiguous()
+    c_q = torch.empty(rows, dq, dtype=bf, device="cuda")
+    q_in = torch.empty(rows, H, dn + dr, dtype=bf, device="cuda")
+    q = torch.empty(rows, H, d.row, dtype=bf, device="cuda")
+    _linear(M, dims, h, w_dq, c_q)
+    _linear(M, dims, c_q, w_uqr, q_in)
+    M.mla_query_absorb(dims, q_in, torch.from_numpy(pos).cuda(), w_uk, q)
+    torch.cuda.synchronize()
+    # each stage against the oracle from the stored bf16 values it was given
+    # (one bf16 rounding each: the element bar holds per stage) ...
+    f = {k: to_f64(t) for k, t in dict(h=h, w_dq=w_dq, w_uq=w_uq, w_qr=w_qr, w_uk=w_uk,
+                                       c_q=c_q, q_in=q_in, q=q).items()}
+    stages = [(f["c_q"], O.linear(f["h"], f["w_dq"])),
+              (f["q_in"][..., :dn], O.linear(f["c_q"], f["w_uq"]).reshape(rows, H, dn)),
+              (f["q_in"][..., dn:], O.linear(f["c_q"], f["w_qr"]).reshape(rows, H, dr)),
+              (f["q"], O.absorb_query(f["q_in"][..., :dn], f["q_in"][..., dn:], f["w_uk"], pos))]
+    for got, ref in stages:
+        assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2
+    # ... and the whole path against the page's unrounded form (three bf16
+    # roundings on the way: c^Q, q_in, q)
+    q_c, q_r = O.query_lowrank(f["h"], f["w_dq"], f["w_uq"], f["w_qr"], H, dn, dr)
+    assert rel_l2(f["q"], O.absorb_query(q_c, q_r, f["w_uk"], pos)) <= 1e-2
+
+
+def test_output_projection_v3():
+    """The module's last step at B = 64: the per-head outputs laid end to end,
+    then W^O [d_model, H d_v]."""
+    import mla_latent_kv_decode_amd as M
+    d, rows = W.V3, 64
+    dims = dims_of(W.CONFIGS["v3"])
+    v = W.normal((rows, d.num_heads, d.d_v), 240, device="cuda", dtype=torch.bfloat16)
+    w_o = W.weight(d.d_model, d.num_heads * d.d_v, 241, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(rows, d.d_model, dtype=torch.bfloat16, device="cuda")
+    _linear(M, dims, v.view(rows, -1), w_o, out)
+    torch.cuda.synchronize()
+    ref = O.output_projection(to_f64(v), to_f64(w_o))
+    assert rel_l2(to_f64(out), ref) <= 1e-2 and max_abs(to_f64(out), ref) <= 2e-2
 
 
 # --------------------------------------------------------------------------

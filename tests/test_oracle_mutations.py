@@ -67,7 +67,28 @@ def _encode_no_saturation(x):
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
+def _lowrank_views_swapped(h, w_dq, w_uq, w_qr, n_heads, d_nope, d_rope):
+    # q^C viewed dimension-major ([d_nope, H] then transposed) instead of head-major
+    c_q = O.linear(h, w_dq)
+    q_c = O.linear(c_q, w_uq)
+    q_r = O.linear(c_q, w_qr)
+    q_c = np.swapaxes(q_c.reshape(q_c.shape[:-1] + (d_nope, n_heads)), -1, -2)
+    return q_c, q_r.reshape(q_r.shape[:-1] + (n_heads, d_rope))
+
+
+def _output_projection_dv_major(v, w_o):
+    v = np.asarray(v, dtype=np.float64)
+    return O.linear(np.swapaxes(v, -1, -2).reshape(v.shape[:-2] + (-1,)), w_o)
+
+
 MUTANTS = {
+    "linear_dropped_last_k": ("linear", lambda x, w: np.asarray(x, np.float64)[..., :-1]
+                              @ np.asarray(w, np.float64)[:, :-1].T,
+                              [P.test_linear_explicit_loops]),
+    "lowrank_query_dim_major_view": ("query_lowrank", _lowrank_views_swapped,
+                                     [P.test_lowrank_query_equals_composed_single_projection]),
+    "output_projection_dv_major": ("output_projection", _output_projection_dv_major,
+                                   [P.test_output_projection_equals_fused_w_ov]),
     "rope_interleaved_pairs": ("rope", _rope_interleaved,
                                [P.test_rope_pairs_channel_j_with_j_plus_half]),
     "rope_sign_flip": ("rope", _rope_sign, [P.test_rope_two_dims_is_textbook_rotation]),

@@ -395,3 +395,57 @@ def test_query_path_absorption_is_associativity():
         lhs = packed[i, :d_c] @ c
         rhs = q_c[i] @ (w_uk[i] @ c)
         assert abs(lhs - rhs) < 1e-12 * (1 + abs(rhs))
+
+
+# --------------------------------------------------------------------------
+# dense layers of the decoding section: low-rank query path, W^O
+# --------------------------------------------------------------------------
+def test_linear_explicit_loops():
+    rng = np.random.default_rng(100)
+    x = rng.standard_normal((3, 7))
+    w = rng.standard_normal((5, 7))     # [n, k]
+    y = O.linear(x, w)
+    assert y.shape == (3, 5)
+    for r in range(3):
+        for n in range(5):
+            assert abs(y[r, n] - sum(x[r, k] * w[n, k] for k in range(7))) < 1e-12
+    # a permutation weight picks input columns
+    perm = [4, 0, 6, 2]
+    np.testing.assert_array_equal(O.linear(x, np.eye(7)[perm]), x[:, perm])
+
+
+def test_lowrank_query_equals_composed_single_projection():
+    """W^UQ (W^DQ h) = (W^UQ W^DQ) h: with the two up-projections' rows put
+    head by head ([W^UQ_i ; W^QR_i]) the product is the single-matrix W^Q of
+    the small workload, split by split_query."""
+    rng = np.random.default_rng(101)
+    H, d_nope, d_r, d_q, d_model = 3, 4, 2, 5, 9
+    w_dq = rng.standard_normal((d_q, d_model))
+    w_uq = rng.standard_normal((H * d_nope, d_q))
+    w_qr = rng.standard_normal((H * d_r, d_q))
+    h = rng.standard_normal((2, d_model))
+    q_c, q_r = O.query_lowrank(h, w_dq, w_uq, w_qr, H, d_nope, d_r)
+    w_q = np.concatenate([np.concatenate([w_uq[i * d_nope:(i + 1) * d_nope],
+                                          w_qr[i * d_r:(i + 1) * d_r]]) for i in range(H)]) @ w_dq
+    c2, r2 = O.split_query(h @ w_q.T, H, d_nope, d_r)
+    np.testing.assert_allclose(q_c, c2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(q_r, r2, rtol=1e-12, atol=1e-12)
+    # head i's content query uses rows i*d_nope .. of W^UQ only
+    c_q = w_dq @ h[1]
+    assert abs(q_c[1, 2, 3] - w_uq[2 * d_nope + 3] @ c_q) < 1e-12
+    assert abs(q_r[1, 1, 0] - w_qr[1 * d_r + 0] @ c_q) < 1e-12
+
+
+def test_output_projection_equals_fused_w_ov():
+    """The offline fusion of [MLA-93] Core Mechanics 3: with W^O_i the
+    columns of W^O that meet head i, sum_i (W^O_i W^UV_i) u_i equals
+    W^O applied to the concatenated W^UV_i u_i."""
+    rng = np.random.default_rng(102)
+    rows, H, d_v, d_c, d = 2, 3, 4, 6, 5
+    u = rng.standard_normal((rows, H, d_c))
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    w_o = rng.standard_normal((d, H * d_v))
+    out = O.output_projection(O.out_proj(u, w_uv), w_o)
+    fused = sum(u[:, i] @ (w_o[:, i * d_v:(i + 1) * d_v] @ w_uv[i]).T for i in range(H))
+    np.testing.assert_allclose(out, fused, rtol=1e-12, atol=1e-12)
+
