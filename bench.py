@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", default="v3", choices=["v3", "long", "ragged", "fp8"])
     p.add_argument("--partitions", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true",
+                   help="skip the separate timing of the query projections and W^O (mla_linear)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--generic", action="store_true", help="force the generic decode kernel")
     p.add_argument("--separate", action="store_true",
@@ -252,6 +254,9 @@ def main():
                 "bytes_alg_per_launch": bytes_alg, "flops_alg_per_launch": flops_alg,
                 "kernel_ms": round(decode_ms, 5)}
 
+    # ---- the dense layers around the step (outside the timed region) -------
+    dense = None if args.no_dense else dense_layers(M, W, dims, d, B * n_q, args.steps, stream)
+
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -276,9 +281,46 @@ def main():
         "launch": "hip_graph_replay" if args.graph else "direct",
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
+        "dense_layers": dense,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def dense_layers(M, W, dims, d, rows, steps, stream):
+    """The decoding procedure's dense layers at this batch, timed on their own
+    (mla_linear): the query projections c^Q = W^DQ h and [W^UQ_i ; W^QR_i] c^Q
+    (head by head, one call), and the output projection W^O.  Each is
+    weight-streaming: the figure is weight bytes per launch / launch time
+    against the HBM peak; two weight copies alternate so the 256 MB Infinity
+    Cache cannot hold the one being read."""
+    import torch
+    H, dq = d.num_heads, d.d_q
+    bf = torch.bfloat16
+    layers = {"w_dq": (d.d_model, dq), "w_uq_qr": (dq, H * (d.d_nope + d.d_rope)),
+              "w_o": (H * d.d_v, d.d_model)}
+    out = {"rows": rows}
+    for j, (name, (k, n)) in enumerate(layers.items()):
+        x = W.normal((rows, k), 500 + j, device="cuda", dtype=bf)
+        ws = [W.weight(n, k, 510 + 2 * j + c, dtype=bf, device="cuda") for c in range(2)]
+        y = torch.empty(rows, n, dtype=bf, device="cuda")
+        nws = M.mla_linear_workspace_size(dims, rows, n, k)
+        wsp = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        for c in range(4):
+            M.mla_linear(dims, x, ws[c % 2], y, wsp)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            evs[i].record(stream)
+            M.mla_linear(dims, x, ws[i % 2], y, wsp)
+        evs[steps].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]))
+        gbps = n * k * 2 / (ms * 1e-3) / 1e9
+        out[name] = {"n": n, "k": k, "ms": round(ms, 5), "weight_gbps": round(gbps, 1),
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        del ws, x, y, wsp
+    return out
 
 
 def cpu_baseline(cfg, pool, sc, table, lens, q_in, w_uk, h, w_dkv, w_kr, w_uv, seconds):
