@@ -6,16 +6,17 @@
 // Matrix-core form (bf16, k a multiple of 512, n of 32).  At decode batch
 // sizes x has few rows and the weight is the stream: every weight byte is
 // read once, as whole 1 KB pieces of its rows.
-//  * One workgroup per (32 weight rows = output columns, up to 64 rows of x,
-//    k range).  Per 512-deep stage its four waves copy the 32 row pieces
-//    into LDS by direct 1 KB loads (the 16-byte chunks of row r XOR-swizzled
-//    by r & 31) while they fetch their x fragments from global memory (x is
-//    small and stays in L2); then each wave runs the MFMAs of its share of
-//    the stage (64 rows: row block w & 1, k half w >> 1; 32 rows: k quarter
-//    w) with the weight fragments read from LDS.  Four workgroups share a
-//    CU, so one's loads overlap another's MFMAs.  (Fragments loaded straight
-//    into registers, 16 bytes per lane from 32 rows at once, streamed the
-//    weight at under a third of this rate.)
+//  * One workgroup per (32 or 64 weight rows = output columns, up to 64 rows
+//    of x, k range).  Per 512-deep stage its four waves copy the weight row
+//    pieces into LDS by direct 1 KB loads (the 16-byte chunks of row r
+//    XOR-swizzled by r & 31) while they fetch their x fragments from global
+//    memory (x is small and stays in L2); then each wave runs the MFMAs of
+//    its share of the stage (64 rows of x: row block w & 1, k half w >> 1;
+//    32 rows: k quarter w) for every 32-column block, the weight fragments
+//    read from LDS.  With 64 columns the x fragments serve two blocks.  Two
+//    or four workgroups share a CU, so one's loads overlap another's MFMAs.
+//    (Fragments loaded straight into registers, 16 bytes per lane from 32
+//    rows at once, streamed the weight at half this rate or less.)
 //  * The waves' 32 x 32 accumulators meet in LDS and are summed in k order;
 //    the workgroup writes y (one k range) or an fp32 partial, which a second
 //    kernel sums over the ranges in range order.  Results are deterministic
@@ -45,7 +46,7 @@ MLA_DEV uint32_t lds_addr(const void* p) {
 
 // kRB 32-row blocks of x and kCB 32-column blocks (weight rows) per workgroup
 template <int kRB, int kCB>
-__global__ __launch_bounds__(kNT, 4 / kCB) void linear_mfma_kernel(LinearArgs a, float* ws, int ks) {
+__global__ __launch_bounds__(kNT, 4 / kCB) void linear_mfma_kernel(LinearArgs a, float* ws, int ks, int row_tiles) {
   constexpr int kCols = kNB * kCB;
   // the weight stage; reused at the end for the cross-wave sums
   __shared__ __attribute__((aligned(1024))) unsigned char wt[kCols * kRowB];
@@ -55,7 +56,12 @@ __global__ __launch_bounds__(kNT, 4 / kCB) void linear_mfma_kernel(LinearArgs a,
   const int g = lane / 32, m = lane % 32;
   const int rb = wave % kRB, kp = wave / kRB;
   const int M = a.rows, K = a.k, N = a.n;
-  const int n0 = blockIdx.x * kCols, split = blockIdx.y, r0 = blockIdx.z * 32 * kRB;
+  // The row tiles of one weight tile are consecutive logical workgroups of
+  // one XCD (workgroups are dealt to the 8 XCDs round-robin), so they run
+  // together and the second reads the weight from that XCD's L2.
+  const int NB = gridDim.x, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;
+  const int n0 = (logical / row_tiles) * kCols, split = blockIdx.y, r0 = (logical % row_tiles) * 32 * kRB;
   const int kb = split * ks, nst = (min(K, kb + ks) - kb) / kStage;
 
   // direct loads of this wave's 8 weight rows: lane l fills chunk slot l of
@@ -220,12 +226,12 @@ size_t linear_mfma_workspace(const LinearArgs& a) {
 
 hipError_t launch_linear_mfma(const LinearArgs& a, void* ws, hipStream_t st) {
   const LinPlan p = linear_plan(a);
-  const dim3 grid(unsigned(a.n / (kNB * p.cb)), unsigned(p.S), unsigned(p.row_tiles));
+  const dim3 grid(unsigned(a.n / (kNB * p.cb) * p.row_tiles), unsigned(p.S));
   float* w = static_cast<float*>(ws);
-  if (p.rb == 1 && p.cb == 1) hipLaunchKernelGGL((linear_mfma_kernel<1, 1>), grid, dim3(kNT), 0, st, a, w, p.ks);
-  if (p.rb == 1 && p.cb == 2) hipLaunchKernelGGL((linear_mfma_kernel<1, 2>), grid, dim3(kNT), 0, st, a, w, p.ks);
-  if (p.rb == 2 && p.cb == 1) hipLaunchKernelGGL((linear_mfma_kernel<2, 1>), grid, dim3(kNT), 0, st, a, w, p.ks);
-  if (p.rb == 2 && p.cb == 2) hipLaunchKernelGGL((linear_mfma_kernel<2, 2>), grid, dim3(kNT), 0, st, a, w, p.ks);
+  if (p.rb == 1 && p.cb == 1) hipLaunchKernelGGL((linear_mfma_kernel<1, 1>), grid, dim3(kNT), 0, st, a, w, p.ks, p.row_tiles);
+  if (p.rb == 1 && p.cb == 2) hipLaunchKernelGGL((linear_mfma_kernel<1, 2>), grid, dim3(kNT), 0, st, a, w, p.ks, p.row_tiles);
+  if (p.rb == 2 && p.cb == 1) hipLaunchKernelGGL((linear_mfma_kernel<2, 1>), grid, dim3(kNT), 0, st, a, w, p.ks, p.row_tiles);
+  if (p.rb == 2 && p.cb == 2) hipLaunchKernelGGL((linear_mfma_kernel<2, 2>), grid, dim3(kNT), 0, st, a, w, p.ks, p.row_tiles);
   if (p.S > 1) {
     const size_t total4 = size_t(a.rows) * a.n / 4;
     hipLaunchKernelGGL(linear_reduce_kernel, dim3(unsigned((total4 + kNT - 1) / kNT)), dim3(kNT), 0, st, a,

@@ -97,6 +97,7 @@ LINEAR_SHAPES = [   # (rows, n, k)
     (33, 96, 1536),         # two row blocks, the second ragged; three stages
     (100, 64, 8192),        # two row tiles, the second ragged; k split in 4
     (7, 64, 1000),          # k % 512 != 0: the VALU form in bf16
+    (150, 192, 1024),       # three row tiles x three column tiles: 9 workgroups over 8 XCDs
 ]
 
 
