@@ -400,16 +400,10 @@ bool combine_out_proj_supported(const CombineProjArgs& a) {
 }
 
 hipError_t launch_combine_out_proj(const CombineProjArgs& a, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(combine_out_proj_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(Smem)));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(combine_out_proj_row_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(RowSmem)));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(combine_out_proj_kernel), int(sizeof(Smem)));
+  if (e == hipSuccess)
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(combine_out_proj_row_kernel), int(sizeof(RowSmem)));
+  if (e != hipSuccess) return e;
   const int R = a.batch * a.n_q;
   if (R <= kMaxRowModeRows) {  // few rows: one workgroup per (head, row)
     hipLaunchKernelGGL(combine_out_proj_row_kernel, dim3(unsigned(a.H) * unsigned(R)), dim3(kNT),

@@ -617,14 +617,10 @@ bool decode_mfma_supported(const DecodeArgs& a) {
 
 template <bool kF8>
 hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t st) {
-  static bool attr_set = false;
   const size_t smem = sizeof(Smem);
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel<kF8>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(decode_mfma_kernel<kF8>), int(smem));
+      e != hipSuccess)
+    return e;
   dim3 grid(unsigned(a.G) * unsigned(a.n_q));
   hipLaunchKernelGGL(decode_mfma_kernel<kF8>, grid, dim3(kNT), smem, st, a);
   return hipGetLastError();

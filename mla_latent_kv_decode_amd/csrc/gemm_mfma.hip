@@ -322,13 +322,10 @@ hipError_t launch_append_mfma(const AppendArgs& a, void* ws, hipStream_t st) {
   int nk, ks;
   append_split(a, &nk, &ks);
   if (append_tiled(a)) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(append_partial_tiled_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(AppTileSmem)));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    if (hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(append_partial_tiled_kernel),
+                                          int(sizeof(AppTileSmem)));
+        e != hipSuccess)
+      return e;
     nk = a.d_model / kTK;
     dim3 g1(unsigned(a.D / kTC), unsigned(nk), unsigned((a.n_tokens + kTT - 1) / kTT));
     hipLaunchKernelGGL(append_partial_tiled_kernel, g1, dim3(kNT), sizeof(AppTileSmem), st, a,

@@ -2,7 +2,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 
 #include "mla_internal.h"
 
@@ -100,6 +103,21 @@ bool linear_use_mfma(const mla_dims* d, const mla::LinearArgs& a) {
   return !(d->flags & MLA_FLAG_GENERIC_DECODE) && a.rows > 0 && mla::linear_mfma_supported(a);
 }
 }  // namespace
+
+namespace mla {
+hipError_t ensure_dynamic_lds(const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({fn, dev});
+  return e;
+}
+}  // namespace mla
 
 extern "C" {
 

@@ -71,6 +71,10 @@ bool query_absorb_mfma_supported(const QueryArgs& a);
 hipError_t launch_query_absorb_mfma(const QueryArgs& a, hipStream_t st);
 hipError_t launch_query_absorb_generic(const QueryArgs& a, hipStream_t st);
 
+// Raises kernel fn's dynamic LDS limit to `bytes` on the current device, once
+// per (kernel, device); safe to call from several host threads.
+hipError_t ensure_dynamic_lds(const void* fn, int bytes);
+
 // y = x W^T
 struct LinearArgs {
   const void* x;           // [rows][k]
