@@ -5,6 +5,7 @@ accumulation -> relative L2 <= 1e-2 and max-abs <= 2e-2; fp8-e4m3 caches ->
 relative L2 <= 5e-2; fp32 workloads are additionally held to 1e-5 relative L2.
 Index and placement work (page tables, slots) is checked bit for bit.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -219,7 +220,7 @@ def _query_case(H, d_nope, d_rope, d_latent, rows, seed, dtype):
     return q_in, w_uk, torch.from_numpy(pos).cuda(), ref
 
 
-@pytest.mark.parametrize("rows", [1, 64, 70])
+@pytest.mark.parametrize("rows", [1, 64, 70, 300])  # 300: RoPE rows in three blocks per workgroup
 def test_query_absorb_v3_bf16(rows):
     import mla_latent_kv_decode_amd as M
     d = W.V3
@@ -510,6 +511,8 @@ MFMA_SMALL = [
     W.scaled(W.CONFIGS["ragged"], batch=6, len_lo=2, len_hi=700),
     W.scaled(W.CONFIGS["v3"], batch=2, seq_len=64),
     W.scaled(W.CONFIGS["v3"], batch=5, seq_len=1),
+    # four causal query tokens per sequence (lengths >= 4)
+    dataclasses.replace(W.scaled(W.CONFIGS["ragged"], batch=3, len_lo=4, len_hi=500), n_q=4),
 ]
 
 
