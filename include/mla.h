@@ -149,6 +149,8 @@ int mla_cache_append(const mla_dims *dims, const void *h, int32_t n_tokens, int3
  * round to nearest even.  bf16 with d_nope = 128, d_latent = 512 and d_rope a
  * multiple of 8 up to 64 (16-byte aligned pointers) runs on the matrix cores;
  * other shapes on a VALU kernel.
+ * Errors: MLA_ERR_INVALID_ARGUMENT (rows < 0, d_nope < 1, a NULL or misaligned
+ * pointer, q_out overlapping q_in); rows = 0 does nothing.
  */
 int mla_query_absorb(const mla_dims *dims, const void *q_in, const int32_t *positions,
                      const void *w_uk, void *q_out, int32_t rows, mla_stream_t stream);

@@ -222,15 +222,13 @@ struct PlanScratch {
   int red[2 * NT / kWave];
 };
 
-// Where the plan reads the sequence lengths from: a global pointer, an LDS
-// copy of all of them, or an LDS window of one chunk of NT sequences that is
-// filled by a direct load when the plan moves to that chunk
-// (lens_stage(src, c) is called by every thread at each chunk start).
+// Where the plan reads the sequence lengths from: a global pointer, or an LDS
+// window of one chunk of NT sequences that is filled by a direct load when the
+// plan moves to that chunk (lens_stage(src, c) is called by every thread at
+// each chunk start).
 typedef __attribute__((address_space(3))) const int32_t lds_len_t;
 MLA_DEV void lens_stage(const int32_t*, int) {}
 MLA_DEV int lens_get(const int32_t* p, int b) { return p[b]; }
-MLA_DEV void lens_stage(lds_len_t*, int) {}
-MLA_DEV int lens_get(lds_len_t* p, int b) { return p[b]; }
 struct LdsLensWindow {
   uint32_t lds;          // LDS byte address of a 1 KB window (256 lengths)
   const int32_t* g;      // the lengths in global memory
