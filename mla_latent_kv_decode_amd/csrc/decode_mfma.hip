@@ -44,7 +44,16 @@
 //    each), 16-byte chunks XOR-swizzled by token so both the b128 K reads and
 //    the transposed V reads spread over all banks.
 //  * The partial is transposed through LDS in the epilogue and written with
-//    whole-row non-temporal stores.
+//    whole-row non-temporal stores.  The partition that owns a sequence's
+//    first cache block also records the sequence's first slot and piece count
+//    in the workspace, where the combine kernels read them.
+//  * Before the plan, the workgroup already streams the Q of the sequence its
+//    first piece would belong to with equal lengths; the plan reads the
+//    lengths from an LDS window loaded ahead of that Q.
+//  * fp8 cache (kF8): each step's e4m3 codes and per-(token, 128-channel)
+//    scales land in a staging buffer and the workgroup dequantises them (code
+//    x scale in fp32, one bf16 rounding) into a bf16 step buffer one
+//    iteration ahead of use; from there the step is read as above.
 #include <utility>
 
 #include "mla_internal.h"

@@ -131,7 +131,10 @@ __global__ __launch_bounds__(kNT) void query_absorb_mfma_kernel(QueryArgs a) {
   //      tile is in flight; staged and written as whole 2 * d_R-byte rows ----
   __bf16* qout = static_cast<__bf16*>(a.q_out);
   {
-    const double inv_freq = rope_inv_freq(tid % max(half, 1), max(half, 1), a.rope_base);  // j = tid % half
+    // the pair index j = (tid + 256 k) % half is tid % half for every k when
+    // half divides 256 (one fp64 power per thread); otherwise it is per k
+    const bool j_fixed = kNT % max(half, 1) == 0;
+    const double inv_freq0 = rope_inv_freq(tid % max(half, 1), max(half, 1), a.rope_base);
     // one block of 32 rows from inputs already in registers (no loads here:
     // a conditional load would make the wave wait for the W tile as well)
     auto emit = [&](int rb, const float (&X)[kRopePerThread], const float (&Z)[kRopePerThread],
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kNT) void query_absorb_mfma_kernel(QueryArgs a) {
         if (it < kRows * half && rb + it / half < rope_rows) {
           const int j = it % half;
           float y0, y1;
-          rope_pair(X[k], Z[k], P[k], inv_freq, &y0, &y1);
+          rope_pair(X[k], Z[k], P[k], j_fixed ? inv_freq0 : rope_inv_freq(j, half, a.rope_base), &y0, &y1);
           reinterpret_cast<__bf16*>(r_lds)[(it / half) * dr + j] = (__bf16)y0;
           reinterpret_cast<__bf16*>(r_lds)[(it / half) * dr + j + half] = (__bf16)y1;
         }

@@ -237,6 +237,26 @@ def test_query_absorb_v3_bf16(rows):
     assert rel_l2(got[..., d.d_latent:], ref[..., d.d_latent:]) <= 4e-3
 
 
+def test_query_absorb_mfma_rope_width_48():
+    """d_R = 48: 24 rotation pairs, which do not divide the workgroup's 256
+    threads (each thread's pairs have different frequencies)."""
+    import mla_latent_kv_decode_amd as M
+    H, dn, dr, dl, rows = 16, 128, 48, 512, 40
+    q_in, w_uk, pos, ref = _query_case(H, dn, dr, dl, rows, 90, torch.bfloat16)
+    outs = []
+    for flags in (0, M.FLAG_GENERIC_DECODE):
+        dims = M.make_dims(H, dl, dr, dn, 128, 64, M.BF16, M.BF16, flags=flags)
+        out = torch.full((rows, H, dl + dr), float("nan"), dtype=torch.bfloat16, device="cuda")
+        M.mla_query_absorb(dims, q_in, pos, w_uk, out)
+        outs.append(to_f64(out))
+    torch.cuda.synchronize()
+    got = outs[0]
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2
+    assert rel_l2(got[..., dl:], ref[..., dl:]) <= 4e-3
+    assert rel_l2(got[..., dl:], outs[1][..., dl:]) <= 1e-4
+
+
 def test_query_absorb_generic_fp32_tight():
     import mla_latent_kv_decode_amd as M
     d = W.TINY
