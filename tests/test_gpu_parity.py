@@ -589,6 +589,41 @@ def test_decode_mfma_agrees_with_generic():
     assert max_abs(l1.cpu().numpy(), l2.cpu().numpy()) <= 1e-3
 
 
+def test_host_threads_on_separate_streams_match_one_thread():
+    """The library keeps no per-call state: two host threads, each launching
+    decode + combine (bf16 and fp8 cache, first use of both kernels included)
+    on its own stream at the same time, get the one-thread results bit for bit."""
+    import threading
+    import mla_latent_kv_decode_amd as M
+    cases = [DecodeCase(W.scaled(W.CONFIGS["v3"], batch=6, seq_len=700)),
+             DecodeCase(W.scaled(W.CONFIGS["fp8"], batch=5, seq_len=400))]
+    outs = [None, None]
+
+    def work(i):
+        c = cases[i]
+        dims = dims_of(c.cfg)
+        B, n_q = c.q.shape[0], c.q.shape[1]
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, 16), dtype=torch.uint8, device="cuda")
+            u = torch.empty(B, n_q, c.d.num_heads, c.d.d_latent, dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty(B, n_q, c.d.num_heads, dtype=torch.float32, device="cuda")
+            for _ in range(3):
+                M.mla_decode(dims, c.q, c.pool, c.scales, c.table_t, c.lens_t, ws, 16, stream=st)
+                M.mla_decode_combine(dims, ws, c.lens_t, u, lse, 16, stream=st)
+        st.synchronize()
+        outs[i] = (u, lse)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    refs = [c.run(G=16) for c in cases]
+    for (u, lse), (ur, lr) in zip(outs, refs):
+        assert torch.equal(u, ur) and torch.equal(lse, lr)
+
+
 def test_decode_mfma_deterministic():
     cfg = W.scaled(W.CONFIGS["ragged"], batch=5, len_lo=100, len_hi=2000)
     case = DecodeCase(cfg)
