@@ -88,6 +88,19 @@ typedef struct mla_dims {
  * cross-checks). */
 #define MLA_FLAG_GENERIC_DECODE 1
 
+/* Validation mode: before its kernels run, a call checks the device-side
+ * preconditions it relies on, with one small kernel and a synchronisation of
+ * `stream`: n_q <= seq_lens[b] (and <= max_blocks_per_seq * block_size where
+ * the call knows it), every page-table entry mla_decode would read >= 0,
+ * positions[t] >= 0 (and < max_blocks_per_seq * block_size for
+ * mla_cache_append), seq_ids[t] >= 0.  On a violation the call returns
+ * MLA_ERR_INVALID_ARGUMENT, names the first offending element in
+ * mla_last_error() and runs nothing.  Not detectable: entries past the
+ * pool's end and sequence ids past the table's rows (neither size is an
+ * argument).  Also on for every call when the environment variable
+ * MLA_VALIDATE is 1.  Checked calls are serialised; meant for debugging. */
+#define MLA_FLAG_VALIDATE 2
+
 int mla_abi_version(void);
 
 /* Description of the last error on the calling thread ("" if none). */

@@ -5,7 +5,7 @@ The computation lives in the HIP library ``libmla.so`` (sources in
 binding.  Build the library with ``python -m mla_latent_kv_decode_amd.build``.
 """
 from ._lib import (  # noqa: F401
-    BF16, EXPORTS, FLAG_GENERIC_DECODE, FP32, FP8_E4M3, LIB_PATH, MlaError, lib, make_dims,
+    BF16, EXPORTS, FLAG_GENERIC_DECODE, FLAG_VALIDATE, FP32, FP8_E4M3, LIB_PATH, MlaError, lib, make_dims,
     mla_abi_version, mla_cache_append, mla_cache_append_workspace_size, mla_decode,
     mla_decode_combine, mla_decode_combine_out_proj, mla_decode_workspace_size,
     mla_device_cu_count, mla_dims, mla_linear, mla_linear_workspace_size, mla_out_proj,

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libmla.so")
 
 FP32, BF16, FP8_E4M3 = 0, 1, 2
 FLAG_GENERIC_DECODE = 1
+FLAG_VALIDATE = 2
 
 OK = 0
 ERR_INVALID_ARGUMENT = -1

@@ -2,6 +2,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <set>
 #include <string>
@@ -83,6 +84,32 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q, int G) {
   w.tab_off = align_up(w.lse_off + slots * size_t(n_q) * d->num_heads * sizeof(float), 256);
   w.total = align_up(w.tab_off + size_t(batch) * 2 * sizeof(int32_t), 256);
   return w;
+}
+
+// Validation mode (MLA_FLAG_VALIDATE, or MLA_VALIDATE=1 in the environment).
+bool validate_on(const mla_dims* d) {
+  static const bool env = [] {
+    const char* v = std::getenv("MLA_VALIDATE");
+    return v && v[0] == '1';
+  }();
+  return env || (d->flags & MLA_FLAG_VALIDATE);
+}
+
+// Runs the device-data checks; MLA_OK, or the error for the first violation.
+int validate(const mla::ValidateArgs& a, mla_stream_t stream) {
+  int out[3] = {0, 0, 0};
+  if (hipError_t e = mla::run_validate(a, static_cast<hipStream_t>(stream), out); e != hipSuccess)
+    return hip_fail(e, "validation");
+  switch (out[0]) {
+    case 0: return MLA_OK;
+    case 1: return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d outside [n_q, max_blocks_per_seq * block_size]",
+                        out[1], out[2]);
+    case 2: return fail(MLA_ERR_INVALID_ARGUMENT, "page-table entry %d read for %s %d is negative", out[2],
+                        a.seq_lens ? "sequence" : "token", out[1]);
+    case 3: return fail(MLA_ERR_INVALID_ARGUMENT, "positions[%d] = %d outside [0, max_blocks_per_seq * block_size)",
+                        out[1], out[2]);
+    default: return fail(MLA_ERR_INVALID_ARGUMENT, "seq_ids[%d] = %d is negative", out[1], out[2]);
+  }
 }
 
 // Shared checks of mla_linear and its workspace query; fills a.
@@ -190,6 +217,10 @@ int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t
   a.cache = cache;
   a.scales = cache_scales;
   a.max_blocks = max_blocks_per_seq;
+  if (validate_on(d))
+    if (int r = validate({nullptr, positions, seq_ids, page_table, n_tokens, 1, max_blocks_per_seq,
+                          d->block_size}, stream))
+      return r;
   hipError_t e;
   if (append_uses_mfma(a)) {
     if (!mla::append_mfma_supported(a))
@@ -260,6 +291,10 @@ int mla_decode(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, con
   a.cache_dtype = d->cache_dtype;
   a.act_dtype = d->act_dtype;
   a.scale = eff_scale(d);
+  if (validate_on(d))
+    if (int r = validate({seq_lens, nullptr, nullptr, page_table, batch, n_q, max_blocks_per_seq, d->block_size},
+                         stream))
+      return r;
   hipError_t e;
   if (!(d->flags & MLA_FLAG_GENERIC_DECODE) && mla::decode_mfma_supported(a)) {
     e = mla::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
@@ -303,6 +338,10 @@ int mla_decode_combine(const mla_dims* d, const void* workspace, size_t workspac
   a.block_size = d->block_size;
   a.G = G;
   a.act_dtype = d->act_dtype;
+  if (validate_on(d))  // lengths only (no page table; no upper bound known here)
+    if (int r = validate({seq_lens, nullptr, nullptr, nullptr, batch, n_q, INT32_MAX / d->block_size, d->block_size},
+                         stream))
+      return r;
   hipError_t e = mla::launch_combine(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
@@ -335,6 +374,8 @@ int mla_query_absorb(const mla_dims* d, const void* q_in, const int32_t* positio
   a.d_latent = d->d_latent;
   a.act_dtype = d->act_dtype;
   a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  if (validate_on(d))  // positions >= 0
+    if (int r = validate({nullptr, positions, nullptr, nullptr, rows, 1, 1, d->block_size}, stream)) return r;
   const bool mfma = !(d->flags & MLA_FLAG_GENERIC_DECODE) && mla::query_absorb_mfma_supported(a);
   hipError_t e = mfma ? mla::launch_query_absorb_mfma(a, static_cast<hipStream_t>(stream))
                       : mla::launch_query_absorb_generic(a, static_cast<hipStream_t>(stream));
@@ -442,6 +483,10 @@ int mla_decode_combine_out_proj(const mla_dims* d, const void* workspace, size_t
   a.d_v = d->d_v;
   a.block_size = d->block_size;
   a.G = G;
+  if (validate_on(d))  // lengths only, as mla_decode_combine
+    if (int r = validate({seq_lens, nullptr, nullptr, nullptr, batch, n_q, INT32_MAX / d->block_size, d->block_size},
+                         stream))
+      return r;
   hipError_t e;
   if (d->act_dtype == MLA_BF16 && mla::combine_out_proj_supported(a)) {
     e = mla::launch_combine_out_proj(a, static_cast<hipStream_t>(stream));

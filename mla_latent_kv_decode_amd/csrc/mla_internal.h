@@ -75,6 +75,18 @@ hipError_t launch_query_absorb_generic(const QueryArgs& a, hipStream_t st);
 // per (kernel, device); safe to call from several host threads.
 hipError_t ensure_dynamic_lds(const void* fn, int bytes);
 
+// Device-data precondition checks (see mla_abi's validation mode): items are
+// sequences (seq_lens given) or tokens (positions given).
+struct ValidateArgs {
+  const int32_t* seq_lens;    // or null
+  const int32_t* positions;   // or null
+  const int32_t* seq_ids;     // with positions and page_table
+  const int32_t* page_table;  // or null: no entry checks
+  int n_items, n_q, max_blocks, block_size;
+};
+// Runs the checks on `st` and waits for them; out = {kind (0: none), item, value}.
+hipError_t run_validate(const ValidateArgs& a, hipStream_t st, int out[3]);
+
 // y = x W^T
 struct LinearArgs {
   const void* x;           // [rows][k]

@@ -589,6 +589,56 @@ def test_decode_mfma_agrees_with_generic():
     assert max_abs(l1.cpu().numpy(), l2.cpu().numpy()) <= 1e-3
 
 
+def test_validation_mode_reports_bad_device_data():
+    """MLA_FLAG_VALIDATE: valid data runs as without the flag (bitwise); a
+    length, page-table entry, position or sequence id that breaks a call's
+    preconditions is reported with its index, and the call runs nothing."""
+    import mla_latent_kv_decode_amd as M
+    from mla_latent_kv_decode_amd import _lib as L
+    case = DecodeCase(W.scaled(W.CONFIGS["v3"], batch=3, seq_len=200))
+    dims = dims_of(case.cfg, M.FLAG_VALIDATE)
+    B, n_q, H = 3, 1, case.d.num_heads
+    ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, 8), dtype=torch.uint8, device="cuda")
+    u = torch.empty(B, n_q, H, case.d.d_latent, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, n_q, H, device="cuda")
+    M.mla_decode(dims, case.q, case.pool, None, case.table_t, case.lens_t, ws, 8)
+    M.mla_decode_combine(dims, ws, case.lens_t, u, lse, 8)
+    ur, lr = case.run(G=8)
+    assert torch.equal(u, ur) and torch.equal(lse, lr)
+
+    def rejected(fn, text):
+        with pytest.raises(M.MlaError) as ei:
+            fn()
+        assert ei.value.code == L.ERR_INVALID_ARGUMENT and text in str(ei.value), str(ei.value)
+
+    cap = case.table.shape[1] * case.d.block_size
+    for b, bad in [(1, 0), (2, cap + 1)]:
+        lens = case.lens_t.clone()
+        lens[b] = bad
+        rejected(lambda: M.mla_decode(dims, case.q, case.pool, None, case.table_t, lens, ws, 8), f"seq_lens[{b}]")
+        if bad == 0:  # the combine knows no upper bound
+            rejected(lambda: M.mla_decode_combine(dims, ws, lens, u, lse, 8), f"seq_lens[{b}]")
+    table = case.table_t.clone()
+    table[1, 2] = -1  # read by sequence 1 (length 200: blocks 0..3)
+    rejected(lambda: M.mla_decode(dims, case.q, case.pool, None, table, case.lens_t, ws, 8), "sequence 1")
+    # token-side calls
+    d = case.d
+    h = W.normal((2, d.d_model), 3, device="cuda", dtype=torch.bfloat16)
+    w_dkv = W.weight(d.d_latent, d.d_model, 4, dtype=torch.bfloat16, device="cuda")
+    w_kr = W.weight(d.d_rope, d.d_model, 5, dtype=torch.bfloat16, device="cuda")
+    aws = append_workspace(dims, 2, d.d_model)
+    for pos, sid, text in [([5, -1], [0, 1], "positions[1]"), ([5, cap], [0, 1], "positions[1]"),
+                           ([5, 6], [-2, 1], "seq_ids[0]")]:
+        rejected(lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, torch.tensor(sid, dtype=torch.int32, device="cuda"),
+                                            torch.tensor(pos, dtype=torch.int32, device="cuda"), case.table_t,
+                                            case.pool, None, aws), text)
+    q_in = W.normal((2, H, d.d_nope + d.d_rope), 6, device="cuda", dtype=torch.bfloat16)
+    w_uk = W.normal((H, d.d_nope, d.d_latent), 7, std=1 / math.sqrt(d.d_latent), device="cuda", dtype=torch.bfloat16)
+    q_out = torch.empty(2, H, d.row, dtype=torch.bfloat16, device="cuda")
+    rejected(lambda: M.mla_query_absorb(dims, q_in, torch.tensor([3, -5], dtype=torch.int32, device="cuda"), w_uk,
+                                        q_out), "positions[1]")
+
+
 def test_host_threads_on_separate_streams_match_one_thread():
     """The library keeps no per-call state: two host threads, each launching
     decode + combine (bf16 and fp8 cache, first use of both kernels included)
