@@ -237,6 +237,10 @@ def main():
     torch.cuda.synchronize()
     per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
     k_ms = per.mean(axis=0)
+    step_ms = per.sum(axis=1)  # per step, events included
+    # the decode and its merge alone (with the fused W^UV when that is one call)
+    dc = [n for n in names if n in ("decode", "combine", "combine_out_proj")]
+    dc_ms = float(sum(k_ms[names.index(n)] for n in dc))
     decode_ms = float(k_ms[names.index("decode")])
 
     # ---- roofline of the dominant kernel (decode) ---------------------------
@@ -277,6 +281,10 @@ def main():
                    "batch": B, "kv_tokens_per_step": kv_tokens, "n_q": n_q,
                    "partitions": G, "pool_copies_rotated": n_copies},
         "kernels_ms": {n: round(float(t), 5) for n, t in zip(names, k_ms)},
+        "evented_step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 5),
+                            "median": round(float(np.median(step_ms)), 5),
+                            "p90": round(float(np.percentile(step_ms, 90)), 5)},
+        "decode_combine_kv_tokens_per_s": {"value": round(kv_tokens / (dc_ms * 1e-3), 1), "calls": dc},
         "decode_kernel": "generic" if args.generic else "default",
         "launch": "hip_graph_replay" if args.graph else "direct",
         "wall_s_timed": round(wall, 4),
