@@ -2,13 +2,15 @@
 """Benchmark of one MLA decode step over a paged latent cache on one MI355X.
 
 A step is one pass of the whole hot path on one batch of synthetic input:
-  mla_cache_append  (B new tokens: W^DKV / W^KR projection, RoPE, paged write)
-  mla_query_absorb  (q~ = W^UK^T q^C and RoPE(q^R) for every query and head)
+  mla_cache_append_query_absorb
+                    (B new tokens: W^DKV / W^KR projection, RoPE, paged write;
+                     and q~ = W^UK^T q^C, RoPE(q^R) for every query and head)
   mla_decode        (split-KV attention over the latent cache, all heads)
   mla_decode_combine_out_proj
                     (log-sum-exp merge of the splits, then the per-head W^UV
-                     up-projection, in one kernel; --separate runs
-                     mla_decode_combine and mla_out_proj as two calls)
+                     up-projection, in one kernel)
+--separate runs the five single calls instead (mla_cache_append,
+mla_query_absorb, mla_decode, mla_decode_combine, mla_out_proj).
 Default workload: DeepSeek-V3 shape, bf16, B=64 sequences of L=4096 cached
 tokens, one query token each, H=128, d_c=512, d_R=64, block 64, shuffled page
 table.  Inputs are resident in HBM before timing; several copies of the pool
@@ -53,8 +55,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--generic", action="store_true", help="force the generic decode kernel")
     p.add_argument("--separate", action="store_true",
-                   help="run mla_decode_combine and mla_out_proj as two calls instead of the "
-                        "fused mla_decode_combine_out_proj")
+                   help="run the five single calls instead of mla_cache_append_query_absorb and "
+                        "mla_decode_combine_out_proj")
     p.add_argument("--graph", action="store_true",
                    help="capture each step (per pool copy) into one HIP graph and replay it")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -167,20 +169,23 @@ def main():
     # The calls of a step, each a closure over one pool copy.
     def calls(i):
         pool, sc = pools[i % n_copies], scales[i % n_copies]
-        head = [
-            lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc, aws),
-            lambda: M.mla_query_absorb(dims, q_in, positions, w_uk, q),
-            lambda: M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G),
-        ]
+        decode = lambda: M.mla_decode(dims, q, pool, sc, table_t, lens_t, ws, G)
         if args.separate:
-            return head + [
+            return [
+                lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool, sc, aws),
+                lambda: M.mla_query_absorb(dims, q_in, positions, w_uk, q),
+                decode,
                 lambda: M.mla_decode_combine(dims, ws, lens_t, u, None, G),
                 lambda: M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o),
             ]
-        return head + [lambda: M.mla_decode_combine_out_proj(dims, ws, lens_t, w_uv, o, B, n_q, None,
-                                                             None, G)]
-    names = ["append", "query_absorb", "decode"] + (["combine", "out_proj"] if args.separate
-                                                     else ["combine_out_proj"])
+        return [
+            lambda: M.mla_cache_append_query_absorb(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, pool,
+                                                    sc, aws, q_in, positions, w_uk, q),
+            decode,
+            lambda: M.mla_decode_combine_out_proj(dims, ws, lens_t, w_uv, o, B, n_q, None, None, G),
+        ]
+    names = (["append", "query_absorb", "decode", "combine", "out_proj"] if args.separate
+             else ["append_query_absorb", "decode", "combine_out_proj"])
 
     for i in range(args.warmup):
         for c in calls(i):

@@ -169,6 +169,31 @@ int mla_query_absorb(const mla_dims *dims, const void *q_in, const int32_t *posi
                      const void *w_uk, void *q_out, int32_t rows, mla_stream_t stream);
 
 /*
+ * mla_cache_append_query_absorb -- mla_cache_append followed by
+ * mla_query_absorb, in fewer launches.  The two operations of a decode step
+ * before the attention ([MLA-93] Core Mechanics 1 and 3 and its decoding
+ * section) do not depend on each other; when both take their matrix-core
+ * forms the append's second step and the query absorption share one launch,
+ * so each one's memory latency hides behind the other's work.
+ * Arguments: those of mla_cache_append (h ... workspace_bytes), then those
+ * of mla_query_absorb (q_in, q_positions = its positions, w_uk, q_out,
+ * q_rows = its rows); each set has the meaning, layout and checks of its own
+ * call, and n_tokens = 0 or q_rows = 0 skips that half.  Results are the
+ * two calls' bit for bit, provided the query's buffers do not overlap the
+ * cache, the scales or the workspace (not checked: the cache's extent is not
+ * an argument).
+ * Errors: those of either call; on an error nothing is launched.
+ */
+int mla_cache_append_query_absorb(const mla_dims *dims, const void *h, int32_t n_tokens,
+                                  int32_t d_model, const void *w_dkv, const void *w_kr,
+                                  const int32_t *seq_ids, const int32_t *positions,
+                                  const int32_t *page_table, int32_t max_blocks_per_seq,
+                                  void *cache, float *cache_scales, void *workspace,
+                                  size_t workspace_bytes, const void *q_in,
+                                  const int32_t *q_positions, const void *w_uk, void *q_out,
+                                  int32_t q_rows, mla_stream_t stream);
+
+/*
  * mla_linear -- y = x W^T, a bias-free linear layer with fp32 accumulation:
  * the query projections of the [MLA-93] decoding section (c^Q = W^DQ h, then
  * q^C = W^UQ c^Q and q^R = W^QR c^Q; placing the rows of W^UQ and W^QR head

@@ -10,4 +10,5 @@ from ._lib import (  # noqa: F401
     mla_decode_combine, mla_decode_combine_out_proj, mla_decode_workspace_size,
     mla_device_cu_count, mla_dims, mla_linear, mla_linear_workspace_size, mla_out_proj,
     mla_query_absorb,
+    mla_cache_append_query_absorb,
 )

@@ -28,7 +28,8 @@ ERR_HIP = -4
 EXPORTS = ("mla_abi_version", "mla_last_error", "mla_device_cu_count",
            "mla_cache_append_workspace_size", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_combine", "mla_out_proj",
-           "mla_decode_combine_out_proj", "mla_query_absorb", "mla_linear_workspace_size",
+           "mla_decode_combine_out_proj", "mla_query_absorb", "mla_cache_append_query_absorb",
+           "mla_linear_workspace_size",
            "mla_linear")
 
 
@@ -89,11 +90,14 @@ def lib():
         L.mla_decode_combine_out_proj.argtypes = [D, _P, ctypes.c_size_t, _I, _I, _P, _I, _P, _P,
                                                   _P, _P, _P]
         L.mla_query_absorb.argtypes = [D, _P, _P, _P, _P, _I, _P]
+        L.mla_cache_append_query_absorb.argtypes = [D, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P,
+                                                    _P, ctypes.c_size_t, _P, _P, _P, _P, _I, _P]
         L.mla_linear_workspace_size.argtypes = [D, _I, _I, _I]
         L.mla_linear_workspace_size.restype = ctypes.c_size_t
         L.mla_linear.argtypes = [D, _P, _I, _I, _P, _I, _P, _P, ctypes.c_size_t, _P]
         for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj",
-                  "mla_decode_combine_out_proj", "mla_query_absorb", "mla_linear"):
+                  "mla_decode_combine_out_proj", "mla_query_absorb", "mla_cache_append_query_absorb",
+                  "mla_linear"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,6 +190,19 @@ def mla_query_absorb(dims, q_in, positions, w_uk, q_out, stream=None):
     rows = q_in.numel() // (dims.num_heads * (dims.d_nope + dims.d_rope))
     _check(lib().mla_query_absorb(ctypes.byref(dims), _ptr(q_in), _ptr(positions), _ptr(w_uk),
                                   _ptr(q_out), rows, _stream(stream)))
+
+
+def mla_cache_append_query_absorb(dims, h, w_dkv, w_kr, seq_ids, positions, page_table, cache,
+                                  cache_scales, workspace, q_in, q_positions, w_uk, q_out, stream=None):
+    """mla_cache_append(dims, h, ..., workspace) then mla_query_absorb(dims, q_in,
+    q_positions, w_uk, q_out), with the arguments of those two calls."""
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rows = q_in.numel() // (dims.num_heads * (dims.d_nope + dims.d_rope))
+    _check(lib().mla_cache_append_query_absorb(
+        ctypes.byref(dims), _ptr(h), h.shape[0], h.shape[1], _ptr(w_dkv), _ptr(w_kr), _ptr(seq_ids),
+        _ptr(positions), _ptr(page_table), page_table.shape[1], _ptr(cache), _ptr(cache_scales),
+        _ptr(workspace), wsb, _ptr(q_in), _ptr(q_positions), _ptr(w_uk), _ptr(q_out), rows,
+        _stream(stream)))
 
 
 def mla_linear_workspace_size(dims, rows: int, n: int, k: int) -> int:

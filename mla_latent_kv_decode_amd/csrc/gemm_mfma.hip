@@ -8,7 +8,7 @@
 // Both are bound by streaming the weights once.  Operands go straight from
 // global memory into the MFMA lane layout (16 contiguous bytes per lane along
 // the reduction), so no LDS staging is needed.
-#include "mla_internal.h"
+#include "append_finalize.h"
 
 namespace mla {
 namespace {
@@ -196,82 +196,11 @@ __global__ __launch_bounds__(kNT) void append_partial_tiled_kernel(AppendArgs a,
   }
 }
 
-// --------------------------------------------------------------------------
-// append, step 2: one 128-thread workgroup per (token, 128-channel tile): sum
-// the k-slice partials of its columns, rotate k^R (rotate-half pairs
-// (j, j + d_R/2), angle pos * base^(-j/(d_R/2)) in fp64, cos/sin rounded to
-// fp32; the host keeps the RoPE part inside one tile), then store in the
-// cache format (e4m3: the tile's amax sets the scale).
-// --------------------------------------------------------------------------
-constexpr int kFinNT = 128;
-
+// append, step 2 (append_finalize.h): two (token, 128-channel tile) units
+// per workgroup.
 template <int CDT>
-__global__ __launch_bounds__(kFinNT) void append_finalize_kernel(AppendArgs a, const float* ws, int nk) {
-  __shared__ float y[kFinNT];
-  __shared__ float wmax[kFinNT / kWave];
-  const int t = blockIdx.x, tile = blockIdx.y, tid = threadIdx.x;
-  const int D = a.D, dc = a.d_latent, T = a.n_tokens;
-  const int c = tile * kFinNT + tid;
-  float v = 0.f;
-  int pos = 0;
-  int64_t row = 0;
-  {
-    // All partials of a chunk are loaded before any is added (unconditional
-    // loads of clamped indices, masked after): one memory round trip per 32
-    // slices; the sum order is fixed (deterministic).  The token's position
-    // and cache row (two dependent scalar lookups) are fetched while the
-    // first chunk is in flight.
-    const float* p = ws + int64_t(t) * D + min(c, D - 1);
-    const int64_t stride = int64_t(T) * D;
-    constexpr int kChunk = 32;
-    for (int kc0 = 0; kc0 < nk; kc0 += kChunk) {
-      float x[kChunk];
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i) x[i] = p[int64_t(min(kc0 + i, nk - 1)) * stride];
-      __builtin_amdgcn_sched_barrier(0);
-      if (kc0 == 0) {
-        pos = a.positions[t];
-        const int blk = a.page_table[int64_t(a.seq_ids[t]) * a.max_blocks + pos / a.block_size];
-        row = int64_t(blk) * a.block_size + pos % a.block_size;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i)
-        if (kc0 + i >= nk) x[i] = 0.f;
-#pragma unroll
-      for (int w = kChunk / 2; w > 0; w /= 2)
-#pragma unroll
-        for (int i = 0; i < w; ++i) x[i] += x[i + w];
-      v += x[0];
-    }
-    if (c >= D) v = 0.f;
-  }
-  y[tid] = v;
-  __syncthreads();
-  const int half = a.d_rope / 2;
-  const int jr = c - dc;
-  if (jr >= 0 && jr < half) {  // this thread owns the pair (jr, jr + half)
-    const double theta = double(pos) * pow(double(a.rope_base), -double(jr) / double(half));
-    const float cs = float(cos(theta)), sn = float(sin(theta));
-    const float x = y[tid], z = y[tid + half];
-    y[tid] = x * cs - z * sn;
-    y[tid + half] = z * cs + x * sn;
-  }
-  __syncthreads();
-  v = y[tid];
-  if constexpr (CDT == MLA_BF16) {
-    if (c < D) static_cast<uint16_t*>(a.cache)[row * D + c] = f32_to_bf16(v);
-  } else if constexpr (CDT == MLA_FP32) {
-    if (c < D) static_cast<float*>(a.cache)[row * D + c] = v;
-  } else {
-    const float am = wave_max(c < D ? fabsf(v) : 0.f);
-    if (tid % kWave == 0) wmax[tid / kWave] = am;
-    __syncthreads();
-    const float amax = fmaxf(wmax[0], wmax[1]);
-    const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
-    if (c < D) static_cast<uint8_t*>(a.cache)[row * D + c] = uint8_t(f32_to_e4m3(__fmul_rn(v, inv)));
-    if (tid == 0) a.scales[row * ((D + 127) / 128) + tile] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  }
+__global__ __launch_bounds__(kNT) void append_finalize_kernel(AppendArgs a, const float* ws, int nk) {
+  append_finalize_pair<CDT>(a, ws, nk, blockIdx.x);
 }
 
 }  // namespace
@@ -311,39 +240,46 @@ bool append_mfma_supported(const AppendArgs& a) {
          (a.d_rope == 0 || (reinterpret_cast<uintptr_t>(a.w_kr) % 16) == 0);
 }
 
-size_t append_mfma_workspace(const AppendArgs& a) {
+int append_mfma_slices(const AppendArgs& a) {
   int nk, ks;
   append_split(a, &nk, &ks);
-  if (append_tiled(a)) nk = a.d_model / kTK;
-  return size_t(nk) * size_t(a.n_tokens) * size_t(a.D) * sizeof(float);
+  return append_tiled(a) ? a.d_model / kTK : nk;
 }
 
-hipError_t launch_append_mfma(const AppendArgs& a, void* ws, hipStream_t st) {
-  int nk, ks;
-  append_split(a, &nk, &ks);
+size_t append_mfma_workspace(const AppendArgs& a) {
+  return size_t(append_mfma_slices(a)) * size_t(a.n_tokens) * size_t(a.D) * sizeof(float);
+}
+
+hipError_t launch_append_partial_mfma(const AppendArgs& a, void* ws, hipStream_t st) {
+  const int nk = append_mfma_slices(a);
   if (append_tiled(a)) {
     if (hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(append_partial_tiled_kernel),
                                           int(sizeof(AppTileSmem)));
         e != hipSuccess)
       return e;
-    nk = a.d_model / kTK;
     dim3 g1(unsigned(a.D / kTC), unsigned(nk), unsigned((a.n_tokens + kTT - 1) / kTT));
     hipLaunchKernelGGL(append_partial_tiled_kernel, g1, dim3(kNT), sizeof(AppTileSmem), st, a,
                        static_cast<float*>(ws));
   } else {
+    int nk_split, ks;  // nk_split == nk for this form
+    append_split(a, &nk_split, &ks);
     dim3 g1(unsigned((a.D + kAppCol - 1) / kAppCol), unsigned(nk), unsigned((a.n_tokens + kAppTok - 1) / kAppTok));
     hipLaunchKernelGGL(append_partial_kernel, g1, dim3(kNT), 0, st, a, static_cast<float*>(ws), ks);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 g2(unsigned(a.n_tokens), unsigned((a.D + kFinNT - 1) / kFinNT));
+  return hipGetLastError();
+}
+
+hipError_t launch_append_mfma(const AppendArgs& a, void* ws, hipStream_t st) {
+  if (hipError_t e = launch_append_partial_mfma(a, ws, st); e != hipSuccess) return e;
+  const int nk = append_mfma_slices(a);
+  const dim3 g2(unsigned((append_finalize_units(a) + 1) / 2));
   const float* w = static_cast<const float*>(ws);
   if (a.cache_dtype == MLA_BF16)
-    hipLaunchKernelGGL(append_finalize_kernel<MLA_BF16>, g2, dim3(kFinNT), 0, st, a, w, nk);
+    hipLaunchKernelGGL(append_finalize_kernel<MLA_BF16>, g2, dim3(kNT), 0, st, a, w, nk);
   else if (a.cache_dtype == MLA_FP32)
-    hipLaunchKernelGGL(append_finalize_kernel<MLA_FP32>, g2, dim3(kFinNT), 0, st, a, w, nk);
+    hipLaunchKernelGGL(append_finalize_kernel<MLA_FP32>, g2, dim3(kNT), 0, st, a, w, nk);
   else
-    hipLaunchKernelGGL(append_finalize_kernel<MLA_FP8_E4M3>, g2, dim3(kFinNT), 0, st, a, w, nk);
+    hipLaunchKernelGGL(append_finalize_kernel<MLA_FP8_E4M3>, g2, dim3(kNT), 0, st, a, w, nk);
   return hipGetLastError();
 }
 

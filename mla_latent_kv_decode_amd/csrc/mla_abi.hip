@@ -188,16 +188,22 @@ size_t mla_cache_append_workspace_size(const mla_dims* d, int32_t n_tokens, int3
   return append_uses_mfma(a) ? mla::append_mfma_workspace(a) : 0;
 }
 
-int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t d_model,
-                     const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
-                     const int32_t* positions, const int32_t* page_table,
-                     int32_t max_blocks_per_seq, void* cache, float* cache_scales,
-                     void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+namespace {
+
+// Argument checks of the cache append.  On success *a holds the call
+// (a->n_tokens == 0: nothing to do) and *mfma says which form runs.
+int append_prepare(const mla_dims* d, const void* h, int32_t n_tokens, int32_t d_model, const void* w_dkv,
+                   const void* w_kr, const int32_t* seq_ids, const int32_t* positions,
+                   const int32_t* page_table, int32_t max_blocks_per_seq, void* cache, float* cache_scales,
+                   void* workspace, size_t workspace_bytes, mla_stream_t stream, mla::AppendArgs* a,
+                   bool* mfma) {
   if (int e = check_dims(d, true)) return e;
   if (n_tokens < 0 || d_model < 1 || max_blocks_per_seq < 1)
     return fail(MLA_ERR_INVALID_ARGUMENT, "n_tokens=%d d_model=%d max_blocks_per_seq=%d", n_tokens,
                 d_model, max_blocks_per_seq);
-  if (n_tokens == 0) return ok();
+  *a = append_args(d, n_tokens, d_model);
+  *mfma = false;
+  if (n_tokens == 0) return MLA_OK;
   if (!h || !w_dkv || !seq_ids || !positions || !page_table || !cache || (d->d_rope > 0 && !w_kr))
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if ((d->cache_dtype == MLA_FP8_E4M3) != (cache_scales != nullptr))
@@ -207,36 +213,125 @@ int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t
       !aligned(seq_ids, 4) || !aligned(positions, 4) || !aligned(page_table, 4) ||
       (cache_scales && !aligned(cache_scales, 4)))
     return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-  mla::AppendArgs a = append_args(d, n_tokens, d_model);
-  a.h = h;
-  a.w_dkv = w_dkv;
-  a.w_kr = w_kr;
-  a.seq_ids = seq_ids;
-  a.positions = positions;
-  a.page_table = page_table;
-  a.cache = cache;
-  a.scales = cache_scales;
-  a.max_blocks = max_blocks_per_seq;
-  if (validate_on(d))
-    if (int r = validate({nullptr, positions, seq_ids, page_table, n_tokens, 1, max_blocks_per_seq,
-                          d->block_size}, stream))
-      return r;
-  hipError_t e;
-  if (append_uses_mfma(a)) {
-    if (!mla::append_mfma_supported(a))
+  a->h = h;
+  a->w_dkv = w_dkv;
+  a->w_kr = w_kr;
+  a->seq_ids = seq_ids;
+  a->positions = positions;
+  a->page_table = page_table;
+  a->cache = cache;
+  a->scales = cache_scales;
+  a->max_blocks = max_blocks_per_seq;
+  if (append_uses_mfma(*a)) {
+    if (!mla::append_mfma_supported(*a))
       return fail(MLA_ERR_INVALID_ARGUMENT, "append: bf16 h / weights must be 16-byte aligned");
-    const size_t need = mla::append_mfma_workspace(a);
+    const size_t need = mla::append_mfma_workspace(*a);
     if (workspace_bytes < need || (need && !workspace))
       return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "append workspace %zu bytes < %zu required",
                   workspace_bytes, need);
     if (!aligned(workspace, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned workspace");
-    e = mla::launch_append_mfma(a, workspace, static_cast<hipStream_t>(stream));
-  } else {
-    if (!mla::append_supported(a))
-      return fail(MLA_ERR_UNSUPPORTED, "append: the RoPE part must lie in one 128-channel tile");
-    e = mla::launch_append(a, static_cast<hipStream_t>(stream));
+    *mfma = true;
+  } else if (!mla::append_supported(*a)) {
+    return fail(MLA_ERR_UNSUPPORTED, "append: the RoPE part must lie in one 128-channel tile");
   }
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  if (validate_on(d))
+    if (int r = validate({nullptr, positions, seq_ids, page_table, n_tokens, 1, max_blocks_per_seq,
+                          d->block_size}, stream))
+      return r;
+  return MLA_OK;
+}
+
+// Argument checks of the query absorption; as above (a->rows == 0: nothing to do).
+int query_prepare(const mla_dims* d, const void* q_in, const int32_t* positions, const void* w_uk, void* q_out,
+                  int32_t rows, mla_stream_t stream, mla::QueryArgs* a, bool* mfma) {
+  if (int e = check_dims(d, false)) return e;
+  if (d->d_nope < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "query absorption needs d_nope >= 1");
+  if (rows < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "rows=%d", rows);
+  a->rows = 0;
+  *mfma = false;
+  if (rows == 0) return MLA_OK;
+  if (!q_in || !positions || !w_uk || !q_out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t ae = elem_bytes(d->act_dtype);
+  if (!aligned(q_in, ae) || !aligned(w_uk, ae) || !aligned(q_out, ae) || !aligned(positions, 4))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  const size_t in_bytes = size_t(rows) * d->num_heads * (d->d_nope + d->d_rope) * ae;
+  const size_t out_bytes = size_t(rows) * d->num_heads * (d->d_latent + d->d_rope) * ae;
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(q_in), o0 = reinterpret_cast<uintptr_t>(q_out);
+  if (i0 < o0 + out_bytes && o0 < i0 + in_bytes)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q_out overlaps q_in");
+  a->q_in = q_in;
+  a->positions = positions;
+  a->w_uk = w_uk;
+  a->q_out = q_out;
+  a->rows = rows;
+  a->H = d->num_heads;
+  a->d_nope = d->d_nope;
+  a->d_rope = d->d_rope;
+  a->d_latent = d->d_latent;
+  a->act_dtype = d->act_dtype;
+  a->rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  *mfma = !(d->flags & MLA_FLAG_GENERIC_DECODE) && mla::query_absorb_mfma_supported(*a);
+  if (validate_on(d))  // positions >= 0
+    if (int r = validate({nullptr, positions, nullptr, nullptr, rows, 1, 1, d->block_size}, stream)) return r;
+  return MLA_OK;
+}
+
+int append_launch(const mla::AppendArgs& a, bool mfma, void* workspace, mla_stream_t stream) {
+  const hipError_t e = mfma ? mla::launch_append_mfma(a, workspace, static_cast<hipStream_t>(stream))
+                            : mla::launch_append(a, static_cast<hipStream_t>(stream));
+  return e != hipSuccess ? hip_fail(e, "append launch") : MLA_OK;
+}
+
+int query_launch(const mla::QueryArgs& a, bool mfma, mla_stream_t stream) {
+  const hipError_t e = mfma ? mla::launch_query_absorb_mfma(a, static_cast<hipStream_t>(stream))
+                            : mla::launch_query_absorb_generic(a, static_cast<hipStream_t>(stream));
+  return e != hipSuccess ? hip_fail(e, "query_absorb launch") : MLA_OK;
+}
+
+}  // namespace
+
+int mla_cache_append(const mla_dims* d, const void* h, int32_t n_tokens, int32_t d_model,
+                     const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
+                     const int32_t* positions, const int32_t* page_table,
+                     int32_t max_blocks_per_seq, void* cache, float* cache_scales,
+                     void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+  mla::AppendArgs a;
+  bool mfma;
+  if (int e = append_prepare(d, h, n_tokens, d_model, w_dkv, w_kr, seq_ids, positions, page_table,
+                             max_blocks_per_seq, cache, cache_scales, workspace, workspace_bytes, stream, &a,
+                             &mfma))
+    return e;
+  if (a.n_tokens > 0)
+    if (int e = append_launch(a, mfma, workspace, stream)) return e;
+  return ok();
+}
+
+int mla_cache_append_query_absorb(const mla_dims* d, const void* h, int32_t n_tokens, int32_t d_model,
+                                  const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
+                                  const int32_t* positions, const int32_t* page_table,
+                                  int32_t max_blocks_per_seq, void* cache, float* cache_scales,
+                                  void* workspace, size_t workspace_bytes, const void* q_in,
+                                  const int32_t* q_positions, const void* w_uk, void* q_out, int32_t q_rows,
+                                  mla_stream_t stream) {
+  mla::AppendArgs ap;
+  mla::QueryArgs q;
+  bool ap_mfma, q_mfma;
+  if (int e = append_prepare(d, h, n_tokens, d_model, w_dkv, w_kr, seq_ids, positions, page_table,
+                             max_blocks_per_seq, cache, cache_scales, workspace, workspace_bytes, stream, &ap,
+                             &ap_mfma))
+    return e;
+  if (int e = query_prepare(d, q_in, q_positions, w_uk, q_out, q_rows, stream, &q, &q_mfma)) return e;
+  if (ap.n_tokens > 0 && q.rows > 0 && ap_mfma && q_mfma) {
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = mla::launch_append_partial_mfma(ap, workspace, st);
+    if (e == hipSuccess) e = mla::launch_append_finalize_query_mfma(ap, workspace, q, st);
+    if (e != hipSuccess) return hip_fail(e, "append + query_absorb launch");
+    return ok();
+  }
+  if (ap.n_tokens > 0)
+    if (int e = append_launch(ap, ap_mfma, workspace, stream)) return e;
+  if (q.rows > 0)
+    if (int e = query_launch(q, q_mfma, stream)) return e;
   return ok();
 }
 
@@ -349,37 +444,11 @@ int mla_decode_combine(const mla_dims* d, const void* workspace, size_t workspac
 
 int mla_query_absorb(const mla_dims* d, const void* q_in, const int32_t* positions, const void* w_uk,
                      void* q_out, int32_t rows, mla_stream_t stream) {
-  if (int e = check_dims(d, false)) return e;
-  if (d->d_nope < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "query absorption needs d_nope >= 1");
-  if (rows < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "rows=%d", rows);
-  if (rows == 0) return ok();
-  if (!q_in || !positions || !w_uk || !q_out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  const size_t ae = elem_bytes(d->act_dtype);
-  if (!aligned(q_in, ae) || !aligned(w_uk, ae) || !aligned(q_out, ae) || !aligned(positions, 4))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-  const size_t in_bytes = size_t(rows) * d->num_heads * (d->d_nope + d->d_rope) * ae;
-  const size_t out_bytes = size_t(rows) * d->num_heads * (d->d_latent + d->d_rope) * ae;
-  const uintptr_t i0 = reinterpret_cast<uintptr_t>(q_in), o0 = reinterpret_cast<uintptr_t>(q_out);
-  if (i0 < o0 + out_bytes && o0 < i0 + in_bytes)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "q_out overlaps q_in");
   mla::QueryArgs a;
-  a.q_in = q_in;
-  a.positions = positions;
-  a.w_uk = w_uk;
-  a.q_out = q_out;
-  a.rows = rows;
-  a.H = d->num_heads;
-  a.d_nope = d->d_nope;
-  a.d_rope = d->d_rope;
-  a.d_latent = d->d_latent;
-  a.act_dtype = d->act_dtype;
-  a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
-  if (validate_on(d))  // positions >= 0
-    if (int r = validate({nullptr, positions, nullptr, nullptr, rows, 1, 1, d->block_size}, stream)) return r;
-  const bool mfma = !(d->flags & MLA_FLAG_GENERIC_DECODE) && mla::query_absorb_mfma_supported(a);
-  hipError_t e = mfma ? mla::launch_query_absorb_mfma(a, static_cast<hipStream_t>(stream))
-                      : mla::launch_query_absorb_generic(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "query_absorb launch");
+  bool mfma;
+  if (int e = query_prepare(d, q_in, positions, w_uk, q_out, rows, stream, &a, &mfma)) return e;
+  if (a.rows > 0)
+    if (int e = query_launch(a, mfma, stream)) return e;
   return ok();
 }
 

@@ -121,6 +121,12 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 bool append_mfma_supported(const AppendArgs& a);
 size_t append_mfma_workspace(const AppendArgs& a);
 hipError_t launch_append_mfma(const AppendArgs& a, void* ws, hipStream_t st);
+int append_mfma_slices(const AppendArgs& a);  // k slices of the matrix-core partials
+hipError_t launch_append_partial_mfma(const AppendArgs& a, void* ws, hipStream_t st);
+// The matrix-core append's second step and the matrix-core query absorption in
+// one launch (they are independent; sharing the GPU hides each one's latency).
+hipError_t launch_append_finalize_query_mfma(const AppendArgs& ap, const void* ws, const QueryArgs& q,
+                                             hipStream_t st);
 hipError_t launch_out_proj_generic(const OutProjArgs& a, hipStream_t st);
 bool out_proj_mfma_supported(const OutProjArgs& a);
 hipError_t launch_out_proj_mfma(const OutProjArgs& a, hipStream_t st);

@@ -25,7 +25,7 @@
 //  * The quarter-cq workgroup also rotates q^R of the rows r = cq (mod 4)
 //    of its head, on the VALU while the W tile is in flight.
 // Other shapes and fp32 run a VALU kernel, one workgroup per (row, head).
-#include "mla_internal.h"
+#include "append_finalize.h"
 
 namespace mla {
 namespace {
@@ -65,7 +65,8 @@ MLA_DEV void rope_pair(float x, float z, int pos, double inv_freq, float* y0, fl
 }
 MLA_DEV double rope_inv_freq(int j, int half, float base) { return pow(double(base), -double(j) / double(half)); }
 
-__global__ __launch_bounds__(kNT) void query_absorb_mfma_kernel(QueryArgs a) {
+// Block blk of NB (NB = 4 H); blk % 8 is the XCD the block runs on.
+MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
   __shared__ __attribute__((aligned(128))) unsigned char w_lds[kMaxNope * kQRow];    // W^UK_i quarter
   __shared__ __attribute__((aligned(128))) unsigned char o_lds[kRows * kQRow];       // output stage
   __shared__ __attribute__((aligned(128))) unsigned char r_lds[kRows * kMaxRope * 2]; // RoPE stage
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kNT) void query_absorb_mfma_kernel(QueryArgs a) {
   const int H = a.H, dn = a.d_nope, dr = a.d_rope, R = a.rows;
   const int in_stride = dn + dr, out_stride = kDL + dr;
   // the four column quarters of one head run on one XCD and share its L2 for q^C
-  const int NB = gridDim.x, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int xcd = blk % 8, idx = blk / 8;
   const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;
   const int h = __builtin_amdgcn_readfirstlane(logical / kQuarters);
   const int cq = __builtin_amdgcn_readfirstlane(logical % kQuarters);
@@ -229,6 +230,21 @@ __global__ __launch_bounds__(kNT) void query_absorb_mfma_kernel(QueryArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kNT) void query_absorb_mfma_kernel(QueryArgs a) {
+  query_absorb_mfma_body(a, blockIdx.x, gridDim.x);
+}
+
+// The same blocks first, then the cache append's second step
+// (append_finalize.h), two units per block, in one launch.
+template <int CDT>
+__global__ __launch_bounds__(kNT) void append_finalize_query_kernel(AppendArgs ap, const float* ws, int nk,
+                                                                    QueryArgs q, int nq) {
+  if (int(blockIdx.x) < nq)
+    query_absorb_mfma_body(q, blockIdx.x, nq);
+  else
+    append_finalize_pair<CDT>(ap, ws, nk, blockIdx.x - nq);
+}
+
 // VALU form: one workgroup per (row, head); thread c accumulates column c.
 template <int ADT>
 __global__ __launch_bounds__(kNT) void query_absorb_generic_kernel(QueryArgs a) {
@@ -277,6 +293,20 @@ bool query_absorb_mfma_supported(const QueryArgs& a) {
 
 hipError_t launch_query_absorb_mfma(const QueryArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(query_absorb_mfma_kernel, dim3(unsigned(a.H) * kQuarters), dim3(kNT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_finalize_query_mfma(const AppendArgs& ap, const void* ws, const QueryArgs& q,
+                                             hipStream_t st) {
+  const int nk = append_mfma_slices(ap), nq = q.H * kQuarters;
+  const dim3 grid(unsigned(nq + (append_finalize_units(ap) + 1) / 2));
+  const float* w = static_cast<const float*>(ws);
+  if (ap.cache_dtype == MLA_BF16)
+    hipLaunchKernelGGL(append_finalize_query_kernel<MLA_BF16>, grid, dim3(kNT), 0, st, ap, w, nk, q, nq);
+  else if (ap.cache_dtype == MLA_FP32)
+    hipLaunchKernelGGL(append_finalize_query_kernel<MLA_FP32>, grid, dim3(kNT), 0, st, ap, w, nk, q, nq);
+  else
+    hipLaunchKernelGGL(append_finalize_query_kernel<MLA_FP8_E4M3>, grid, dim3(kNT), 0, st, ap, w, nk, q, nq);
   return hipGetLastError();
 }
 

@@ -154,6 +154,26 @@ def test_query_absorb_validates(L):
     assert call(ctypes.byref(no_nope)) == L.ERR_INVALID_ARGUMENT
 
 
+def test_append_query_absorb_validates_both_halves(L):
+    """The one-call form rejects what either of its two calls rejects, before
+    launching anything, and does nothing when both halves are empty."""
+    lib = L.lib()
+    d = _dims(L)
+    need = L.mla_cache_append_workspace_size(d, 4, 7168)
+    call = lambda T=4, sc=None, ws=FAKE, wsb=need, q=FAKE * 64, out=FAKE * 128, rows=2: \
+        lib.mla_cache_append_query_absorb(ctypes.byref(d), FAKE, T, 7168, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                          FAKE, sc, ws, wsb, q, FAKE, FAKE, out, rows, None)
+    assert call(sc=FAKE) == L.ERR_INVALID_ARGUMENT                 # the append half: scales on bf16
+    assert call(wsb=need - 1) == L.ERR_WORKSPACE_TOO_SMALL
+    assert call(T=-1) == L.ERR_INVALID_ARGUMENT
+    assert call(rows=-1) == L.ERR_INVALID_ARGUMENT                 # the query half
+    assert call(q=None) == L.ERR_INVALID_ARGUMENT
+    assert call(out=FAKE * 64 + 256) == L.ERR_INVALID_ARGUMENT      # q_out overlapping q_in
+    assert "overlap" in lib.mla_last_error().decode()
+    assert call(T=0, rows=0) == L.OK
+    assert call(T=0, rows=-1) == L.ERR_INVALID_ARGUMENT
+
+
 def test_linear_validates_and_sizes_its_workspace(L):
     lib = L.lib()
     d = _dims(L)

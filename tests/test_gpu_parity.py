@@ -419,6 +419,61 @@ def test_append_v3_fp8_random_weights(T):
     assert rel_l2(np.stack(got), want) <= 5e-2
 
 
+@pytest.mark.parametrize("cache_dtype,act,flags,T,rows", [
+    ("bf16", "bf16", 0, 64, 64),   # one shared launch
+    ("fp8", "bf16", 0, 33, 70),    # 165 append units: the last workgroup's second half is idle
+    ("fp32", "bf16", 0, 1, 300),
+    ("bf16", "bf16", 0, 0, 5),     # no tokens: the query half alone
+    ("fp8", "bf16", 0, 7, 0),      # no query rows: the append half alone
+    ("fp32", "fp32", 0, 5, 3),     # VALU forms, two launches
+    ("bf16", "bf16", 1, 9, 9),     # VALU query form beside the matrix-core append
+])
+def test_append_query_absorb_one_call_matches_two_calls(cache_dtype, act, flags, T, rows):
+    """mla_cache_append_query_absorb writes the cache rows, fp8 scales and
+    absorbed queries of mla_cache_append followed by mla_query_absorb, bit for
+    bit (those two calls are held to the oracle above)."""
+    import mla_latent_kv_decode_amd as M
+    d = W.V3
+    cfg = dataclasses.replace(W.CONFIGS["v3"], cache_dtype=cache_dtype, act_dtype=act)
+    dims = dims_of(cfg, flags)
+    adt = torch.bfloat16 if act == "bf16" else torch.float32
+    cdt = {"bf16": torch.bfloat16, "fp32": torch.float32, "fp8": torch.uint8}[cache_dtype]
+    h = W.normal((T, d.d_model), 70 + T, device="cuda").to(adt)
+    w_dkv = W.weight(d.d_latent, d.d_model, 71, dtype=adt, device="cuda")
+    w_kr = W.weight(d.d_rope, d.d_model, 72, dtype=adt, device="cuda")
+    lens = np.full(max(T, 1), 300, np.int32)
+    table, nblk = W.page_table(lens, 64, seed=7, guard_blocks=1)
+    positions = _t(np.random.default_rng(T).integers(0, 300, T).astype(np.int32), torch.int32)
+    seq_ids = torch.arange(T, dtype=torch.int32, device="cuda")
+    table_t = _t(table, torch.int32)
+    q_in = W.normal((rows, d.num_heads, d.d_nope + d.d_rope), 73 + rows, device="cuda").to(adt)
+    w_uk = W.normal((d.num_heads, d.d_nope, d.d_latent), 74, std=1 / math.sqrt(d.d_latent),
+                    device="cuda").to(adt)
+    q_pos = _t(np.random.default_rng(rows).integers(0, 131072, rows).astype(np.int32), torch.int32)
+    ws = append_workspace(dims, max(T, 1), d.d_model)
+
+    def run(one_call):
+        cache = torch.zeros((nblk, 64, d.row), dtype=cdt, device="cuda")
+        scales = torch.zeros((nblk, 64, 5), device="cuda") if cache_dtype == "fp8" else None
+        q_out = torch.full((rows, d.num_heads, d.row), float("nan"), dtype=adt, device="cuda")
+        if one_call:
+            M.mla_cache_append_query_absorb(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, cache, scales,
+                                            ws, q_in, q_pos, w_uk, q_out)
+        else:
+            M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, cache, scales, ws)
+            M.mla_query_absorb(dims, q_in, q_pos, w_uk, q_out)
+        torch.cuda.synchronize()
+        out = [cache.view(torch.uint8), q_out.view(torch.uint8)]
+        return out + ([scales.view(torch.uint8)] if scales is not None else [])
+
+    two, one = run(False), run(True)
+    for a, b in zip(two, one):
+        assert torch.equal(a, b)
+    assert torch.isfinite(one[1].view(adt).float()).all()
+    if T:
+        assert bool(one[0].any())
+
+
 # --------------------------------------------------------------------------
 # decode + combine
 # --------------------------------------------------------------------------
