@@ -692,6 +692,15 @@ def test_validation_mode_reports_bad_device_data():
     q_out = torch.empty(2, H, d.row, dtype=torch.bfloat16, device="cuda")
     rejected(lambda: M.mla_query_absorb(dims, q_in, torch.tensor([3, -5], dtype=torch.int32, device="cuda"), w_uk,
                                         q_out), "positions[1]")
+    # the one-call form checks both halves
+    good_pos = torch.tensor([5, 6], dtype=torch.int32, device="cuda")
+    sids = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    pool0 = case.pool.clone()
+    rejected(lambda: M.mla_cache_append_query_absorb(dims, h, w_dkv, w_kr, sids, good_pos, case.table_t, case.pool,
+                                                     None, aws, q_in, torch.tensor([3, -5], dtype=torch.int32,
+                                                                                   device="cuda"), w_uk, q_out),
+             "positions[1]")
+    assert torch.equal(case.pool.view(torch.int16), pool0.view(torch.int16))  # rejected before the append ran
 
 
 def test_host_threads_on_separate_streams_match_one_thread():
@@ -817,8 +826,8 @@ def test_combine_out_proj_matches_separate_calls_and_oracle(idx):
 # the step captured into HIP graphs (how bench.py and a serving loop run it)
 # --------------------------------------------------------------------------
 def test_graph_replay_matches_eager():
-    """append + decode + combine + out_proj captured as HIP graphs and replayed
-    three times, with eager work on the stream between replays: every replay
+    """append + query absorption (one call) + decode + combine + out_proj
+    captured as HIP graphs and replayed three times, with eager work on the stream between replays: every replay
     reproduces the eager outputs bit for bit (the calls allocate nothing and
     record no memsets, so they are safe to capture)."""
     import mla_latent_kv_decode_amd as M
@@ -843,9 +852,13 @@ def test_graph_replay_matches_eager():
     positions = (case.lens_t.repeat_interleave(n_q) - n_q
                  + torch.arange(n_q, dtype=torch.int32, device=dev).repeat(B)).to(torch.int32)
     aws = append_workspace(dims, T, d.d_model)
+    q_in = W.normal((T, H, d.d_nope + d.d_rope), 45, device=dev, dtype=torch.bfloat16)
+    w_uk = W.normal((H, d.d_nope, d.d_latent), 46, std=1 / math.sqrt(d.d_latent), device=dev,
+                    dtype=torch.bfloat16)
+    qa = torch.empty(T, H, d.row, dtype=torch.bfloat16, device=dev)  # absorbed queries of the new tokens
     calls = [
-        lambda: M.mla_cache_append(dims, h, w_dkv, w_kr, seq_ids, positions, case.table_t,
-                                   case.pool, None, aws),
+        lambda: M.mla_cache_append_query_absorb(dims, h, w_dkv, w_kr, seq_ids, positions, case.table_t,
+                                                case.pool, None, aws, q_in, positions, w_uk, qa),
         lambda: M.mla_decode(dims, case.q, case.pool, None, case.table_t, case.lens_t, ws, G),
         lambda: M.mla_decode_combine(dims, ws, case.lens_t, u, lse, G),
         lambda: M.mla_out_proj(dims, u.view(B * n_q, H, d.d_latent), w_uv, o),
@@ -854,7 +867,7 @@ def test_graph_replay_matches_eager():
         c()
     torch.cuda.synchronize()
     bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
-    ref = [bits(x).clone() for x in (u, lse, o, case.pool)]
+    ref = [bits(x).clone() for x in (u, lse, o, case.pool, qa)]
     assert torch.isfinite(o.float()).all()
     cap = torch.cuda.Stream()
     graphs = []
@@ -864,10 +877,10 @@ def test_graph_replay_matches_eager():
             c()
         graphs.append(g)
     for rep in range(3):
-        for x in (u, lse, o, ws):
+        for x in (u, lse, o, ws, qa):
             x.zero_()  # eager work between replays
         for g in graphs:
             g.replay()
         torch.cuda.synchronize()
-        for got, want in zip((u, lse, o, case.pool), ref):
+        for got, want in zip((u, lse, o, case.pool, qa), ref):
             assert torch.equal(bits(got), want), f"replay {rep} differs from the eager run"
