@@ -182,7 +182,7 @@ int mla_query_absorb(const mla_dims *dims, const void *q_in, const int32_t *posi
  * two calls' bit for bit, provided the query's buffers do not overlap the
  * cache, the scales or the workspace (not checked: the cache's extent is not
  * an argument).
- * Errors: those of either call; on an error nothing is launched.
+ * Errors: those of either call; on an error neither operation runs.
  */
 int mla_cache_append_query_absorb(const mla_dims *dims, const void *h, int32_t n_tokens,
                                   int32_t d_model, const void *w_dkv, const void *w_kr,
