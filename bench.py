@@ -45,8 +45,8 @@ BYTES_PER_KV_TOKEN = {"bf16": 1152, "fp8": 596, "fp32": 2304}
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="v3", choices=["v3", "long", "ragged", "fp8"])
     p.add_argument("--partitions", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
