@@ -14,7 +14,10 @@ namespace mla {
 
 constexpr int kFinNT = 128;  // threads per unit (one per channel of the tile)
 
-static __host__ __device__ inline int append_finalize_units(const AppendArgs& a) { return a.n_tokens * ((a.D + kFinNT - 1) / kFinNT); }
+// (token, 128-channel tile) units of a call
+static __host__ __device__ inline int append_finalize_units(const AppendArgs& a) {
+  return a.n_tokens * ((a.D + kFinNT - 1) / kFinNT);
+}
 
 // Units 2 * pair and 2 * pair + 1 (unit u = token u / tiles, tile u % tiles).
 // A half past the last unit recomputes the last one and stores nothing.
