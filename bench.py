@@ -90,7 +90,7 @@ def traffic_from_profile(kernel_src: str, workload: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs the whole hot path on a single "
+        print(f"bench.py measures one GPU only: the library runs the whole hot path on a single "
               f"MI355X (no sharding, no collectives); got --gpus {args.gpus}", file=sys.stderr)
         sys.exit(2)
 
