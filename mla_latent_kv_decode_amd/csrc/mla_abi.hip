@@ -514,8 +514,6 @@ int mla_out_proj(const mla_dims* d, const void* u, int32_t rows, const void* w_u
   return ok();
 }
 
-}  // extern "C"
-
 int mla_decode_combine_out_proj(const mla_dims* d, const void* workspace, size_t workspace_bytes,
                                 int32_t batch, int32_t n_q, const int32_t* seq_lens,
                                 int32_t num_partitions, const void* w_uv, void* out, void* u_out,
@@ -570,3 +568,5 @@ int mla_decode_combine_out_proj(const mla_dims* d, const void* workspace, size_t
     return r;
   return mla_out_proj(d, u_out, batch * n_q, w_uv, out, stream);
 }
+
+}  // extern "C"

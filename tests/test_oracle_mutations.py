@@ -81,7 +81,45 @@ def _output_projection_dv_major(v, w_o):
     return O.linear(np.swapaxes(v, -1, -2).reshape(v.shape[:-2] + (-1,)), w_o)
 
 
+def _dequant_tile0_scale(codes, scales):
+    # every tile decoded with tile 0's scale
+    c = np.asarray(codes)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return O.e4m3_decode(c) * s[..., 0:1]
+
+
+def _dequant_tiles_of_64(codes, scales):
+    # tile boundaries every 64 channels instead of 128
+    c = np.asarray(codes)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    out = O.e4m3_decode(c)
+    for k in range(c.shape[-1] // 64):
+        out[..., 64 * k:64 * k + 64] *= s[..., min(k, s.shape[-1] - 1):min(k, s.shape[-1] - 1) + 1]
+    return out
+
+
+_orig_absorb_query = O.absorb_query
+
+
+def _absorb_unrotated(q_c, q_r, w_uk, pos, base=10000.0):
+    return _orig_absorb_query(q_c, q_r, w_uk, np.zeros_like(np.asarray(pos)), base)
+
+
+def _absorb_first_row_position(q_c, q_r, w_uk, pos, base=10000.0):
+    p = np.asarray(pos)
+    return _orig_absorb_query(q_c, q_r, w_uk, np.full_like(p, p.flat[0]) if p.ndim else p, base)
+
+
 MUTANTS = {
+    "fp8_dequant_tile0_scale": ("dequantize_fp8_rows", _dequant_tile0_scale,
+                                [P.test_dequantize_fp8_rows_per_tile_scales]),
+    "fp8_dequant_tiles_of_64": ("dequantize_fp8_rows", _dequant_tiles_of_64,
+                                [P.test_dequantize_fp8_rows_per_tile_scales]),
+    "absorb_query_rope_unrotated": ("absorb_query", _absorb_unrotated,
+                                    [P.test_absorbed_query_rope_half_is_rotated_at_each_rows_position]),
+    "absorb_query_rope_first_row_position": (
+        "absorb_query", _absorb_first_row_position,
+        [P.test_absorbed_query_rope_half_is_rotated_at_each_rows_position]),
     "linear_dropped_last_k": ("linear", lambda x, w: np.asarray(x, np.float64)[..., :-1]
                               @ np.asarray(w, np.float64)[:, :-1].T,
                               [P.test_linear_explicit_loops]),

@@ -449,3 +449,87 @@ def test_output_projection_equals_fused_w_ov():
     fused = sum(u[:, i] @ (w_o[:, i * d_v:(i + 1) * d_v] @ w_uv[i]).T for i in range(H))
     np.testing.assert_allclose(out, fused, rtol=1e-12, atol=1e-12)
 
+
+
+# --------------------------------------------------------------------------
+# fp8 dequantisation and the rotated half of the packed query
+# --------------------------------------------------------------------------
+# (code, value) pairs of the OCP E4M3 encoding, read off its bit layout by
+# hand: sign, 4 exponent bits (bias 7), 3 mantissa bits, subnormals m * 2^-9.
+E4M3_KNOWN = [(0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+              (0x30, 0.5), (0x38, 1.0), (0x3C, 1.5), (0x40, 2.0), (0x4B, 5.5),
+              (0x7E, 448.0), (0xB8, -1.0), (0xC4, -3.0), (0xFE, -448.0)]
+
+
+def test_dequantize_fp8_rows_per_tile_scales():
+    """Each channel decodes to its code's value times the scale of its own
+    128-channel tile; the row's last tile (channels 512..575) is half width.
+    The expected values are the listed code values times a scale chosen
+    distinct for every (row, tile) -- powers of two and non-dyadic ones -- so
+    a tile boundary off by any amount, or one tile's scale reused for another,
+    changes some element."""
+    rng = np.random.default_rng(110)
+    n_rows, D = 3, 576
+    pick = rng.integers(0, len(E4M3_KNOWN), size=(n_rows, D))
+    codes = np.array([[E4M3_KNOWN[k][0] for k in r] for r in pick], dtype=np.uint8)
+    vals = np.array([[E4M3_KNOWN[k][1] for k in r] for r in pick], dtype=np.float64)
+    # tile k of row r: 2^(k - 2) * (1 + r / 3), written out per tile
+    scales = np.array([[np.float32(2.0 ** (k - 2) * (1 + r / 3)) for k in range(5)]
+                       for r in range(n_rows)], dtype=np.float32)
+    got = O.dequantize_fp8_rows(codes, scales)
+    assert got.shape == (n_rows, D)
+    for r in range(n_rows):
+        for c in range(D):
+            tile = 0 if c < 128 else 1 if c < 256 else 2 if c < 384 else 3 if c < 512 else 4
+            want = vals[r, c] * float(scales[r, tile])
+            assert got[r, c] == want, (r, c, got[r, c], want)
+    # leading axes (blocks x tokens) broadcast the same way
+    got3 = O.dequantize_fp8_rows(codes.reshape(1, n_rows, D), scales.reshape(1, n_rows, 5))
+    assert np.array_equal(got3[0], got)
+
+
+def test_absorbed_query_rope_half_is_rotated_at_each_rows_position():
+    """packed[..., d_c:] of absorb_query is q^R rotated at the row's own
+    position.  With d_R = 2 the rotation is the textbook 2-D rotation by
+    pos radians (the only frequency is base^0 = 1); the positions differ per
+    row, so a broadcast of one row's position, an unrotated q^R or a rotation
+    at position 0 all fail.  The content half is checked against explicit
+    sums of q^C_i[n] W^UK_i[n, c]."""
+    rng = np.random.default_rng(111)
+    rows, H, d_nope, d_c = 4, 3, 5, 6
+    pos = np.array([[0], [1], [7], [131071]], dtype=np.int64)[:, 0]
+    for d_r in (2, 8):
+        q_c = rng.standard_normal((rows, H, d_nope))
+        q_r = rng.standard_normal((rows, H, d_r))
+        w_uk = rng.standard_normal((H, d_nope, d_c))
+        packed = O.absorb_query(q_c, q_r, w_uk, pos)
+        assert packed.shape == (rows, H, d_c + d_r)
+        for r in range(rows):
+            for i in range(H):
+                for c in range(d_c):
+                    want = sum(q_c[r, i, n] * w_uk[i, n, c] for n in range(d_nope))
+                    assert abs(packed[r, i, c] - want) <= 1e-12 * (1 + abs(want))
+                if d_r == 2:
+                    th = float(pos[r])
+                    R = np.array([[math.cos(th), -math.sin(th)], [math.sin(th), math.cos(th)]])
+                    np.testing.assert_allclose(packed[r, i, d_c:], R @ q_r[r, i], rtol=0, atol=1e-12)
+                else:
+                    # each pair (j, j + 4) is turned by pos * 10000^(-j/4)
+                    for j in range(d_r // 2):
+                        th = float(pos[r]) * 10000.0 ** (-j / (d_r // 2))
+                        x, y = q_r[r, i, j], q_r[r, i, j + d_r // 2]
+                        assert abs(packed[r, i, d_c + j] - (x * math.cos(th) - y * math.sin(th))) <= 1e-9
+                        assert abs(packed[r, i, d_c + j + d_r // 2]
+                                   - (y * math.cos(th) + x * math.sin(th))) <= 1e-9
+    # a [B, n_q] position grid (the decode's query layout) rotates each query at its own position
+    q_c = rng.standard_normal((2, 2, H, d_nope))
+    q_r = rng.standard_normal((2, 2, H, 2))
+    w_uk = rng.standard_normal((H, d_nope, d_c))
+    grid = np.array([[10, 11], [500, 501]])
+    packed = O.absorb_query(q_c, q_r, w_uk, grid)
+    for b in range(2):
+        for j in range(2):
+            th = float(grid[b, j])
+            R = np.array([[math.cos(th), -math.sin(th)], [math.sin(th), math.cos(th)]])
+            for i in range(H):
+                np.testing.assert_allclose(packed[b, j, i, d_c:], R @ q_r[b, j, i], rtol=0, atol=1e-12)
