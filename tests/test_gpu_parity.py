@@ -547,21 +547,109 @@ def test_out_proj_v3_bf16():
 
 
 # --------------------------------------------------------------------------
-# full-size workloads, default launch configuration, sampled sequences
+# full-size workloads, default launch configuration
 # --------------------------------------------------------------------------
-FULL = {"v3": [0, 17, 63], "long": [0, 3], "fp8": [0, 77, 127]}
+TWO_GIB = 1 << 31
+
+
+def _ragged_sample(case, n=16):
+    """n sequences spread over the length range (every len-rank n-th), plus
+    the sequence that owns the highest physical block, so that some compared
+    sequence reads cache blocks at byte offsets past 2^31."""
+    order = np.argsort(case.lens, kind="stable")
+    pick = set(int(order[i]) for i in np.linspace(0, len(order) - 1, n).round().astype(int))
+    owner = int(np.argwhere(case.table == case.table.max())[0, 0])
+    pick.add(owner)
+    return sorted(pick)
+
+
+FULL = {"v3": lambda c: list(range(64)), "long": lambda c: [0, 1, 2, 3],
+        "fp8": lambda c: list(range(0, 128, 4)), "ragged": _ragged_sample}
 
 
 @pytest.mark.parametrize("name", sorted(FULL))
-def test_full_size_sampled(name):
+def test_full_size(name):
+    """Every config at its full size in the default launch configuration:
+    all sequences of v3 and long, 32 of fp8, and 17 of ragged (lengths from
+    the shortest to the longest, the 2.29 GB pool's last block included)."""
     cfg = W.CONFIGS[name]
     case = DecodeCase(cfg)
+    ids = FULL[name](case)
+    if name == "ragged":
+        row_bytes = case.d.block_size * case.d.row * 2
+        assert case.nblk * row_bytes > TWO_GIB
+        hi = [b for b in ids if int(case.table[b].max()) * row_bytes >= TWO_GIB]
+        assert hi, "no compared sequence reads past 2 GiB"
     u, lse = case.run()
     if cfg.cache_dtype == "fp8":
-        compare_sampled(case, u, lse, FULL[name], rel_bar=5e-2, abs_bar=None)
+        compare_sampled(case, u, lse, ids, rel_bar=5e-2, abs_bar=None)
     else:
-        compare_sampled(case, u, lse, FULL[name])
-    assert torch.isfinite(u.float()).all()
+        compare_sampled(case, u, lse, ids)
+    assert torch.isfinite(u.float()).all() and torch.isfinite(lse).all()
+
+
+def test_full_v3_benchmark_step():
+    """The benchmark's step exactly as bench.py runs it at the full v3 shape
+    (B = 64, L = 4096, default partitions): the one-call append + query
+    absorption, the decode, the fused merge + W^UV.  The appended rows, the
+    absorbed queries, u and o are each checked against the oracle, for all
+    64 sequences."""
+    import mla_latent_kv_decode_amd as M
+    cfg = W.CONFIGS["v3"]
+    case = DecodeCase(cfg)
+    d = case.d
+    dev = "cuda"
+    B, n_q, H = cfg.batch, cfg.n_q, d.num_heads
+    dims = dims_of(cfg)
+    T = B * n_q
+    h = W.normal((T, d.d_model), 61, device=dev, dtype=torch.bfloat16)
+    w_dkv = W.weight(d.d_latent, d.d_model, 62, dtype=torch.bfloat16, device=dev)
+    w_kr = W.weight(d.d_rope, d.d_model, 63, dtype=torch.bfloat16, device=dev)
+    q_in = W.normal((B, n_q, H, d.d_nope + d.d_rope), 64, device=dev, dtype=torch.bfloat16)
+    w_uk = W.normal((H, d.d_nope, d.d_latent), 65, std=1 / math.sqrt(d.d_latent), device=dev,
+                    dtype=torch.bfloat16)
+    w_uv = W.normal((H, d.d_v, d.d_latent), 66, std=1 / math.sqrt(d.d_latent), device=dev,
+                    dtype=torch.bfloat16)
+    seq_ids = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(n_q)
+    positions = (case.lens_t.repeat_interleave(n_q) - n_q
+                 + torch.arange(n_q, dtype=torch.int32, device=dev).repeat(B)).to(torch.int32)
+    aws = append_workspace(dims, T, d.d_model)
+    q = torch.empty(B, n_q, H, d.row, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(M.mla_decode_workspace_size(dims, B, n_q, 0), dtype=torch.uint8, device=dev)
+    o = torch.full((T, H, d.d_v), float("nan"), dtype=torch.bfloat16, device=dev)
+    u = torch.full((B, n_q, H, d.d_latent), float("nan"), dtype=torch.bfloat16, device=dev)
+    pool0 = case.pool.clone()
+    M.mla_cache_append_query_absorb(dims, h, w_dkv, w_kr, seq_ids, positions, case.table_t, case.pool,
+                                    None, aws, q_in, positions, w_uk, q)
+    M.mla_decode(dims, q, case.pool, None, case.table_t, case.lens_t, ws, 0)
+    M.mla_decode_combine_out_proj(dims, ws, case.lens_t, w_uv, o, B, n_q, u, None, 0)
+    torch.cuda.synchronize()
+    # appended rows: only the new tokens' slots changed, each within bf16 rounding
+    pos = positions.cpu().numpy()
+    rows_ref = O.kv_rows(to_f64(h), to_f64(w_dkv), to_f64(w_kr), pos)
+    changed = (case.pool.view(torch.int16) != pool0.view(torch.int16)).any(dim=-1).cpu().numpy()
+    want = np.zeros_like(changed)
+    got_rows = []
+    for t in range(T):
+        blk, off = O.slot_of(case.table, t // n_q, int(pos[t]), d.block_size)
+        want[blk, off] = True
+        got_rows.append(to_f64(case.pool[blk, off]))
+    assert not np.any(changed & ~want), "a slot other than the new tokens' was written"
+    got_rows = np.stack(got_rows)
+    assert rel_l2(got_rows, rows_ref) <= 1e-2 and max_abs(got_rows, rows_ref) <= 2e-2
+    # absorbed queries
+    qi = to_f64(q_in)
+    q_ref = O.absorb_query(qi[..., :d.d_nope], qi[..., d.d_nope:], to_f64(w_uk),
+                           pos.reshape(B, n_q))
+    assert rel_l2(to_f64(q), q_ref) <= 1e-2 and max_abs(to_f64(q), q_ref) <= 2e-2
+    # u and o, from the stored q and the cache as the append left it
+    case.q = q
+    u_ref = np.stack([case.oracle(b)[0] for b in range(B)])
+    assert rel_l2(to_f64(u), u_ref) <= 1e-2 and max_abs(to_f64(u), u_ref) <= 2e-2
+    o_ref = O.out_proj(u_ref.reshape(T, H, d.d_latent), to_f64(w_uv))
+    got = to_f64(o)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, o_ref) <= 1e-2 and max_abs(got, o_ref) <= 2e-2
 
 
 # --------------------------------------------------------------------------
@@ -771,6 +859,11 @@ FUSED = [
     (W.scaled(W.CONFIGS["ragged"], batch=5, len_lo=2, len_hi=3000), 64),    # up to ~30 pieces a row
     (W.scaled(W.CONFIGS["ragged"], batch=20, len_lo=2, len_hi=3000), 64),   # 40 rows, many pieces
     (W.scaled(W.CONFIGS["long"], batch=4, seq_len=16384), 256),             # 4 rows x 64 pieces
+    # several 32-row groups per workgroup (the default above 96 rows): W^UV_i
+    # loaded once and reused, per-group reads of the slot table
+    (W.scaled(W.CONFIGS["v3"], batch=128, seq_len=200), 0),                 # 128 rows: 2 groups each
+    (W.scaled(W.CONFIGS["ragged"], batch=256, len_lo=2, len_hi=600), 0),   # 512 rows, n_q = 2: 8 groups
+    (W.scaled(W.CONFIGS["v3"], batch=200, seq_len=130), 0),                 # 7 groups, 3 per workgroup: last has 1
 ]
 ROW_MODE_MAX_ROWS = 32  # the fused kernel gives each (head, row) its own workgroup up to here
 
