@@ -296,6 +296,35 @@ int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
                                 const void *w_uv, void *out, void *u_out, float *lse_out,
                                 mla_stream_t stream);
 
+/*
+ * mla_decode_noalloc -- mla_decode followed by mla_decode_combine, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Instead of a
+ * caller workspace, the partials live in a device array that the library
+ * owns: MLA_NOALLOC_SCRATCH_BYTES (64 MiB) on every device the library runs
+ * on, held until the process ends.  The call allocates and frees nothing.
+ *   Arguments: those of mla_decode (without workspace / workspace_bytes),
+ *   then u_out [batch][n_q][num_heads][d_latent] act_dtype (required) and
+ *   lse_out [batch][n_q][num_heads] fp32 (may be NULL) as in
+ *   mla_decode_combine.  Results equal the two calls' with the same
+ *   num_partitions, bit for bit.
+ * Limit: the call needs mla_decode_workspace_size(dims, batch, n_q,
+ * num_partitions) <= MLA_NOALLOC_SCRATCH_BYTES; larger calls return
+ * MLA_ERR_WORKSPACE_TOO_SMALL and run nothing (e.g. H = 128, d_latent = 512,
+ * bf16: (batch + partitions) * n_q <= 509).
+ * Every call on one device shares that device's array: calls that overlap
+ * in time on one device (two streams, two threads) race and give undefined
+ * results; calls ordered on one stream are safe.  The first call on each
+ * device looks the array's address up (thread-safe).
+ * Errors: those of mla_decode and mla_decode_combine, plus the above.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int mla_decode_noalloc(const mla_dims *dims, const void *q, int32_t batch, int32_t n_q,
+                       const void *cache, const float *cache_scales, const int32_t *page_table,
+                       int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t num_partitions,
+                       void *u_out, float *lse_out, mla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,8 @@ EXPORTS = ("mla_abi_version", "mla_last_error", "mla_device_cu_count",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_combine", "mla_out_proj",
            "mla_decode_combine_out_proj", "mla_query_absorb", "mla_cache_append_query_absorb",
            "mla_linear_workspace_size",
-           "mla_linear")
+           "mla_linear", "mla_decode_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MlaError(RuntimeError):
@@ -95,9 +96,10 @@ def lib():
         L.mla_linear_workspace_size.argtypes = [D, _I, _I, _I]
         L.mla_linear_workspace_size.restype = ctypes.c_size_t
         L.mla_linear.argtypes = [D, _P, _I, _I, _P, _I, _P, _P, ctypes.c_size_t, _P]
+        L.mla_decode_noalloc.argtypes = [D, _P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _P]
         for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj",
                   "mla_decode_combine_out_proj", "mla_query_absorb", "mla_cache_append_query_absorb",
-                  "mla_linear"):
+                  "mla_linear", "mla_decode_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -218,3 +220,13 @@ def mla_linear(dims, x, w, y, workspace=None, stream=None):
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_linear(ctypes.byref(dims), _ptr(x), rows, k, _ptr(w), w.shape[0], _ptr(y),
                             _ptr(workspace), wsb, _stream(stream)))
+
+
+def mla_decode_noalloc(dims, q, cache, cache_scales, page_table, seq_lens, u_out, lse_out=None,
+                       num_partitions: int = 0, stream=None):
+    """mla_decode + mla_decode_combine with the library's static scratch as the
+    workspace.  q [B, n_q, H, D]; u_out [B, n_q, H, d_latent]; lse_out [B, n_q, H] or None."""
+    _check(lib().mla_decode_noalloc(ctypes.byref(dims), _ptr(q), q.shape[0], q.shape[1], _ptr(cache),
+                                    _ptr(cache_scales), _ptr(page_table), page_table.shape[1],
+                                    _ptr(seq_lens), num_partitions, _ptr(u_out), _ptr(lse_out),
+                                    _stream(stream)))

@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <map>
 #include <mutex>
 #include <set>
 #include <string>
@@ -128,6 +129,36 @@ int linear_args(const mla_dims* d, const void* x, int32_t rows, int32_t k, const
 }
 bool linear_use_mfma(const mla_dims* d, const mla::LinearArgs& a) {
   return !(d->flags & MLA_FLAG_GENERIC_DECODE) && a.rows > 0 && mla::linear_mfma_supported(a);
+}
+
+
+// ---------------------------------------------------------------------------
+// Library-owned decode workspace for callers that cannot allocate
+// (mla_decode_noalloc).  One copy per device, alive until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// is only a stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(MLA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call per device, thread-safe).  MLA_OK or MLA_ERR_HIP.
+int noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return MLA_OK;
 }
 }  // namespace
 
@@ -567,6 +598,29 @@ int mla_decode_combine_out_proj(const mla_dims* d, const void* workspace, size_t
                                  num_partitions, u_out, lse_out, stream))
     return r;
   return mla_out_proj(d, u_out, batch * n_q, w_uv, out, stream);
+}
+
+int mla_decode_noalloc(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, const void* cache,
+                       const float* cache_scales, const int32_t* page_table, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, int32_t num_partitions, void* u_out, float* lse_out,
+                       mla_stream_t stream) {
+  if (int e = check_dims(d, true)) return e;
+  if (batch < 0 || n_q < 1 || num_partitions > MLA_MAX_PARTITIONS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d n_q=%d num_partitions=%d", batch, n_q, num_partitions);
+  if (batch == 0) return ok();
+  const size_t need = mla_decode_workspace_size(d, batch, n_q, num_partitions);
+  if (need > kNoAllocScratchBytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "mla_decode_noalloc: this call needs %zu bytes of decode workspace, the library's static "
+                "scratch holds %zu (use fewer sequences, query tokens or partitions, or mla_decode with a "
+                "caller workspace)", need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (int e = noalloc_scratch(&ws)) return e;
+  if (int e = mla_decode(d, q, batch, n_q, cache, cache_scales, page_table, max_blocks_per_seq, seq_lens,
+                         num_partitions, ws, kNoAllocScratchBytes, stream))
+    return e;
+  return mla_decode_combine(d, ws, kNoAllocScratchBytes, batch, n_q, seq_lens, num_partitions, u_out,
+                            lse_out, stream);
 }
 
 }  // extern "C"
