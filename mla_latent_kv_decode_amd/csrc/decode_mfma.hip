@@ -31,12 +31,15 @@
 //    AGPRs (256 per lane) and keeps one head per lane, so the epilogue needs
 //    no cross-lane traffic.
 //  * Softmax in log2 units against a per-head reference m_ref taken from the
-//    head's first step: p = 2^(s' - m_ref).  While later scores stay below
-//    m_ref + kHeadroom (32), p <= 2^32 and nothing can overflow in fp32 or
-//    bf16, so O is only ever touched by MFMA.  A head that exceeds it moves
-//    its reference to the new maximum and its wave rescales O and the running
-//    sum by 2^(old - new) (the exact online-softmax update; it does not
-//    happen for ordinary logits).
+//    head's first step: p = 2^(s' - m_ref).  While a lane's 16 values of a
+//    step sum to at most 2^32, nothing can overflow in fp32 or bf16, so O is
+//    only ever touched by MFMA and no per-step maximum is needed.  A step
+//    whose sum exceeds that is redone against its maximum, and the wave
+//    rescales O and the running sum by 2^(old - new) (the exact online-softmax
+//    update; it does not happen for ordinary logits).
+//  * Instruction issue, not the matrix cores or LDS, bounds the step loop (one
+//    wave per SIMD issues in order and nothing hides its stalls): the loop
+//    keeps per-step scalar and VALU work, branches and full waits small.
 //  * Masked (past-length) tokens: their score is -inf, and their rows lie
 //    outside the load's buffer range, which fills them with zeros, so
 //    0 * (stale value / NaN) never reaches the accumulators.
@@ -78,7 +81,9 @@ constexpr int kF8Loads = kF8Codes / 1024;            // 18 direct loads of codes
 constexpr int kLdsBytes = (kNBuf * kStepBytes > kF8NBuf * kStepBytes + 2 * kF8Stage)
                               ? kNBuf * kStepBytes : kF8NBuf * kStepBytes + 2 * kF8Stage;
 constexpr int kLoadsPerWave = 9;              // 1 KB direct loads per wave per step
-constexpr float kHeadroom = 32.0f;            // log2 headroom above the reference max
+// A lane's 16 probabilities of a step summing past this (2^32) left the
+// headroom above the reference: the step is recomputed against its maximum.
+constexpr float kPSumLimit = 4294967296.0f;
 constexpr int kStageRow = kDC * 2 + 16;       // epilogue transpose row (padded against bank conflicts)
 constexpr int kQK = kD / 16;                  // score MFMAs per step
 constexpr int kPV = 2 * (kDC / 32);           // output MFMAs per step
@@ -92,7 +97,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 // 16-byte-chunk swizzle: chunk slot (c & 7) ^ swz(t) within token t's sub-row.
 MLA_DEV int swz(int t) { return ((((t & 3) << 1) | ((t >> 2) & 1)) ^ ((t >> 2) & 2)) & 7; }
@@ -102,12 +106,19 @@ MLA_DEV int step_off(int t, int c) {
   return (((t >> 3) * 9 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz(t))) * 16;
 }
 
+constexpr int kPtab = 1024;  // page-table entries of a piece staged in LDS at a time
+
 struct Smem {
   // bf16 step buffer i at i * kStepBytes (kStepBytes is a multiple of 128);
   // for the fp8 cache, staging buffer i follows the three step buffers
   alignas(128) unsigned char lds[kLdsBytes];
   PlanScratch<kNT> plan;
   alignas(16) int32_t lens[256];  // window of sequence lengths for the plan
+  // The piece's physical block ids, blocks [pbase, pbase + kPtab): the step
+  // loop reads them from here instead of issuing scalar loads.  A scalar load
+  // in flight completes out of order, so every wait for an LDS operand behind
+  // it would have to wait for it too (lgkmcnt(0)) -- once per step.
+  alignas(16) int32_t ptab[kPtab];
 };
 
 // Wait until at most N of this wave's vector-memory operations are pending.
@@ -150,15 +161,27 @@ MLA_DEV void load_one(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, in
                : "v"(loff), "s"(r), "s"(wave * 9216 + M * 128), "{m0}"(lds)
                : "memory");
 }
+// Load m (0..8) of this wave's share of a step (runtime m, same as load_one<m>).
+MLA_DEV void load_piece(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, int loff, int m) {
+  const int k = wave * kLoadsPerWave + m;
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) unsigned char*)(dst + k * 1024)));
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(loff), "s"(r), "s"(wave * 9216 + m * 128), "{m0}"(lds)
+               : "memory");
+}
 template <int... Ms>
 MLA_DEV void load_all(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, int loff,
                       std::integer_sequence<int, Ms...>) {
   (load_one<Ms>(r, dst, wave, loff), ...);
 }
+// Descriptor of one step's rows in the cache: only the live rows are in range.
+MLA_DEV __amdgpu_buffer_rsrc_t step_rsrc(const unsigned char* src, int nvalid) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nvalid * kRowBytes, 0x00020000);
+}
 MLA_DEV void load_step(unsigned char* dst, const unsigned char* src, int nvalid, int wave, int loff) {
-  __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nvalid * kRowBytes, 0x00020000);
-  load_all(r, dst, wave, loff, std::make_integer_sequence<int, kLoadsPerWave>{});
+  load_all(step_rsrc(src, nvalid), dst, wave, loff, std::make_integer_sequence<int, kLoadsPerWave>{});
 }
 
 // One fp8 step into a staging buffer: the 32 rows of e4m3 codes are one
@@ -364,8 +387,17 @@ void decode_mfma_kernel(DecodeArgs a) {
       if (elane < 32) a.ws_lse[orow0 + elane] = -INFINITY;
       return;
     }
-    // page table through the constant address space: scalar loads
-    const_i32* pt = (const_i32*)(uintptr_t)(a.page_table + int64_t(b) * a.max_blocks);
+    // the piece's row of the page table (vector loads into sm.ptab)
+    const int32_t* pt = a.page_table + int64_t(b) * a.max_blocks + ulo;
+    const int nblk_need = (nsteps + 1) >> 1;  // blocks holding the piece's visible steps
+    auto fill_ptab = [&](int base) __attribute__((always_inline)) {
+      const int n = min(kPtab, nblk_need - base);
+      for (int i = tid_fresh(); i < n; i += kNT) sm.ptab[i] = pt[base + i];
+    };
+    int pbase = 0;  // first block of the piece held in sm.ptab (wave-uniform)
+    auto block_of = [&](int i) __attribute__((always_inline)) {  // physical block of the piece's block i
+      return __builtin_amdgcn_readfirstlane(sm.ptab[i - pbase]);
+    };
     const unsigned char* cache = static_cast<const unsigned char*>(a.cache);
     auto step_at = [&](int blk, int h) {  // first byte of step h, which lies in block blk
       return cache + int64_t(blk) * kBlockBytes + (h & 1) * kStepBytes;
@@ -376,7 +408,6 @@ void decode_mfma_kernel(DecodeArgs a) {
                    a.scales + (int64_t(blk) * kBS + (h & 1) * kStep) * 5, nvalid, wave, lane);
     };
     auto valid_in = [&](int h) { return min(kStep, t_hi - (t_lo + h * kStep)); };
-    const int blk0 = pt[ulo];  // steps 0 and 1 lie in the piece's first block
 
     // Q^T fragments for this wave's 32 heads, resident for the whole piece.
     // The 32 heads' rows of a wave are one contiguous 36 KB block -- a step
@@ -386,8 +417,10 @@ void decode_mfma_kernel(DecodeArgs a) {
     // instead of 16-byte pieces of 32 rows per instruction.
     if (!(q_pre && b == b_pre)) load_q(b);
     q_pre = false;
+    fill_ptab(0);  // in flight together with Q
     wait_vm<0>();
     step_barrier();
+    const int blk0 = block_of(0);  // steps 0 and 1 lie in the piece's first block
     bf16x8 qf[kQK];
     {
       // (addresses from a fresh lane id: not kept live across the step loop)
@@ -416,7 +449,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     // V^T . P^T for step h-1 (32 MFMAs), with the softmax of step h spread
     // between them, so the exp/max VALU work runs under matrix work.  The
     // first step has no PV yet; the drain after the last step has no QK.
-    auto run_step = [&](auto qk_on, auto pv_on, int h) __attribute__((always_inline)) {
+    auto run_step = [&](auto qk_on, auto pv_on, int h, auto&& after_qk_mfma) __attribute__((always_inline)) {
       constexpr bool kQKOn = decltype(qk_on)::value, kPVOn = decltype(pv_on)::value;
       const uint32_t kb = lds_addr(bbuf(h % NB)) + koff0_at();
       const uint32_t vb = lds_addr(bbuf(h > 0 ? (h + NB - 1) % NB : 0)) + voff0_at();
@@ -438,7 +471,10 @@ void decode_mfma_kernel(DecodeArgs a) {
       if constexpr (kQKOn) {
         bf16x8 kr[kRK];
 #pragma unroll
-        for (int n = 0; n < kRK; ++n) kr[n] = kfrag(n);
+        for (int n = 0; n < kRK; ++n) {  // in order: the first MFMA waits only for the first read
+          kr[n] = kfrag(n);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int n = 0; n < kQK; ++n) {
           if (n == 0)
@@ -451,6 +487,7 @@ void decode_mfma_kernel(DecodeArgs a) {
             const int v = n + kRK - kQK;
             if (v < kRV) vr[v] = vfrag(v);
           }
+          after_qk_mfma(n);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
@@ -458,10 +495,15 @@ void decode_mfma_kernel(DecodeArgs a) {
         for (int n = 0; n < kRV; ++n) vr[n] = vfrag(n);
       }
 
-      // softmax of step h in pieces (lane = one head; tokens 8*(r/4) + 4*g + r%4)
+      // softmax of step h in pieces (lane = one head; tokens 8*(r/4) + 4*g + r%4):
+      // p = 2^(s' - m_ref) against the head's current reference, without
+      // first taking the step's maximum.  Whether a p left the headroom is
+      // read off the lane's sum of its 16 values afterwards (> 2^32, inf or
+      // NaN); that -- and the piece's first step, whose reference is still
+      // -inf -- takes the exact path below, which recomputes the step against
+      // its maximum.
       const int nv = kQKOn ? valid_in(h) : kStep;
-      float mx = 0.f, lsum = 0.f, corr = 1.f;
-      bool spike = false;
+      float lsum = 0.f, lsum2 = 0.f;
       auto softmax_part = [&](int k) __attribute__((always_inline)) {
         if constexpr (kQKOn) {
           if (k == 0) scores_ready(S);
@@ -470,30 +512,16 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) S[r] = (8 * (r / 4) + (r % 4) >= lim) ? -INFINITY : S[r];
           }
-          if (k == 2) {
-            mx = S[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-          }
-          if (k == 3) {
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c_log2;
-            // the piece's first step sets the head's reference; a later step
-            // more than kHeadroom above it moves it (and rescales O below)
-            spike = m_ref != -INFINITY && mx > m_ref + kHeadroom;
-            const float m_new = m_ref == -INFINITY || spike ? mx : m_ref;
-            corr = spike ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-            m_ref = m_new;
-          }
-          if (k >= 4 && k < 12) {
-            const int i = (k - 4) >> 2, e = 2 * ((k - 4) & 3);
+          if (k >= 2 && k < 10) {
+            const int i = (k - 2) >> 2, e = 2 * ((k - 2) & 3);
             const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_log2, -m_ref));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e + 1], c_log2, -m_ref));
-            lsum += p0;
-            lsum += p1;
+            lsum += p0;   // two running sums: half the dependent chain
+            lsum2 += p1;
             p_cur[i][e / 2] = pack_bf16x2(p0, p1);
             // pin the work here, between the output MFMAs: left alone, the
             // compiler sinks it to the end of the step where nothing hides it
-            asm volatile("" : "+v"(p_cur[i][e / 2]), "+v"(lsum));
+            asm volatile("" : "+v"(p_cur[i][e / 2]), "+v"(lsum), "+v"(lsum2));
           }
         }
       };
@@ -508,18 +536,46 @@ void decode_mfma_kernel(DecodeArgs a) {
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 12; ++k) softmax_part(k);
+        for (int k = 0; k < 10; ++k) softmax_part(k);
       }
       if constexpr (kQKOn) {
-        if (__any(spike)) {  // rare: rescale this wave's accumulated output
-          o_ready(O);
+        if (h == 0 || __any(!(lsum + lsum2 <= kPSumLimit))) {
+          // Exact path: the step's maximum per head (the other 16 tokens of
+          // the head sit in lane ^ 32: a lane-half swap), the reference moved
+          // to it, and the step's p recomputed.  On a later step (a score far
+          // above the reference) the wave's accumulated output and sum are
+          // rescaled by 2^(old - new): the exact online-softmax update.
+          const float a0 = fmaxf(fmaxf(S[0], S[1]), S[2]), a1 = fmaxf(fmaxf(S[3], S[4]), S[5]);
+          const float a2 = fmaxf(fmaxf(S[6], S[7]), S[8]), a3 = fmaxf(fmaxf(S[9], S[10]), S[11]);
+          const float a4 = fmaxf(fmaxf(S[12], S[13]), S[14]);
+          float mx = fmaxf(fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)), fmaxf(a4, S[15]));
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c_log2;
+          const float m_new = h == 0 ? mx : fmaxf(m_ref, mx);
+          const float corr = h == 0 ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+          m_ref = m_new;
+          lsum = lsum2 = 0.f;
 #pragma unroll
-          for (int cb = 0; cb < kDC / 32; ++cb) {
-            O[cb] *= corr;                        // through VGPRs ...
-            asm volatile("" : "+a"(O[cb]));       // ... and back into the AGPRs
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_log2, -m_ref));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e + 1], c_log2, -m_ref));
+              lsum += p0;
+              lsum2 += p1;
+              p_cur[i][e / 2] = pack_bf16x2(p0, p1);
+            }
+          if (h != 0) {  // (wave-uniform) O holds earlier steps: rescale it
+            o_ready(O);
+#pragma unroll
+            for (int cb = 0; cb < kDC / 32; ++cb) {
+              O[cb] *= corr;                        // through VGPRs ...
+              asm volatile("" : "+a"(O[cb]));       // ... and back into the AGPRs
+            }
           }
+          l_run *= corr;
         }
-        l_run = l_run * corr + lsum;
+        l_run += lsum + lsum2;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
           p_prev[i] = __builtin_bit_cast(bf16x8, u32x4{p_cur[i][0], p_cur[i][1], p_cur[i][2], p_cur[i][3]});
@@ -527,28 +583,57 @@ void decode_mfma_kernel(DecodeArgs a) {
     };
 
     // block of the next step to prefetch, looked up one step early
-    int blk_nx = nsteps > 2 ? pt[ulo + 1] : 0;
+    int blk_nx = nsteps > 2 ? block_of(1) : 0;
+    // Past the staged window of the page table, every wave first refills
+    // sm.ptab (at most once per kPtab blocks: a piece longer than 65536
+    // tokens).  Called right after a step barrier, when no wave still reads
+    // the old window.
+    auto ptab_window = [&](int i) __attribute__((always_inline)) {
+      if (i - pbase >= kPtab) {
+        wait_vm<0>();
+        pbase += kPtab;
+        fill_ptab(pbase);
+        step_barrier();
+      }
+    };
+    auto next_block = [&](int h) __attribute__((always_inline)) {  // the block of step h + 3
+      ptab_window((h + 3) >> 1);
+      blk_nx = block_of((h + 3) >> 1);
+    };
+    auto no_hook = [](int) __attribute__((always_inline)) {};
     if constexpr (!kF8) {
       if (nsteps > 1) load_step(bbuf(1), step_at(blk0, 1), valid_in(1), wave, loff);
-      // Step h waits until its own loads are done (at most the loads of step
-      // h+1, issued one iteration earlier, still pending), then a barrier makes
-      // every wave's share visible and frees buffer (h+2)%4 for the next load.
-      auto begin_step = [&](int h) __attribute__((always_inline)) {
+      // Iteration h: wait until step h's own loads are done (at most the loads
+      // of step h+1, issued one iteration earlier, still pending); a barrier
+      // makes every wave's share visible and frees buffer (h+2)%4.  The K
+      // fragments of step h are read first; the nine loads of step h+2 are
+      // spread over the score MFMAs (issued back to back by all four waves
+      // at once, they would queue on the compute unit's address unit for
+      // several hundred cycles).  The page-table entry of step h+3 is read
+      // from LDS here and resolved one iteration later, so its latency is
+      // never waited for on its own.
+      int blk_raw = 0;  // sm.ptab entry of step h+2, read in iteration h-1
+      for (int h = 0; h < nsteps; ++h) {
         if (h + 1 < nsteps)
           wait_vm<kLoadsPerWave>();
         else
           wait_vm<0>();
         step_barrier();
-        if (h + 2 < nsteps)
-          load_step(bbuf((h + 2) % kNBuf), step_at(blk_nx, h + 2), valid_in(h + 2), wave, loff);
-        if (h + 3 < nsteps) blk_nx = pt[ulo + ((h + 3) >> 1)];
-      };
-      // Step 0 runs the same code with P = 0 against its own (finite, zero-filled
-      // past the length) buffer: a second specialisation without PV costs the
-      // register allocator more than these 32 MFMAs cost the piece.
-      for (int h = 0; h < nsteps; ++h) {
-        begin_step(h);
-        run_step(std::true_type{}, std::true_type{}, h);
+        if (h > 0) blk_nx = __builtin_amdgcn_readfirstlane(blk_raw);
+        const bool nx = h + 3 < nsteps;
+        if (nx) ptab_window((h + 3) >> 1);
+        // past the last step the descriptor is empty: the nine loads still run
+        // (no branch around each) and only write zeros into a free buffer
+        const bool ld = h + 2 < nsteps;
+        const __amdgpu_buffer_rsrc_t r = step_rsrc(ld ? step_at(blk_nx, h + 2) : cache, ld ? valid_in(h + 2) : 0);
+        unsigned char* const dst = bbuf((h + 2) % kNBuf);
+        // Step 0 runs the same code with P = 0 against its own (finite,
+        // zero-filled past the length) buffer: a second specialisation without
+        // PV costs the register allocator more than these 32 MFMAs cost.
+        run_step(std::true_type{}, std::true_type{}, h, [&](int n) __attribute__((always_inline)) {
+          if (n % 4 == 1) load_piece(r, dst, wave, loff, n / 4);
+          if (n == 2 && nx) blk_raw = sm.ptab[((h + 3) >> 1) - pbase];
+        });
       }
     } else {
       // fp8: step h's codes land in staging buffer h%2 and are dequantised
@@ -566,8 +651,8 @@ void decode_mfma_kernel(DecodeArgs a) {
       for (int h = 0; h < nsteps; ++h) {
         step_barrier();  // step h converted; staging buffer h%2 free again
         if (h + 2 < nsteps) load_f8(h & 1, blk_nx, h + 2, valid_in(h + 2));
-        if (h + 3 < nsteps) blk_nx = pt[ulo + ((h + 3) >> 1)];
-        run_step(std::true_type{}, std::true_type{}, h);
+        if (h + 3 < nsteps) next_block(h);
+        run_step(std::true_type{}, std::true_type{}, h, no_hook);
         if (h + 1 < nsteps) {
           if (h + 2 < nsteps)
             wait_vm<4>();
@@ -578,7 +663,8 @@ void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     }
-    run_step(std::false_type{}, std::true_type{}, nsteps);  // PV of the last step
+    run_step(std::false_type{}, std::true_type{}, nsteps, no_hook);  // PV of the last step
+    wait_vm<0>();  // the last iterations' empty loads, before the LDS is reused
     o_ready(O);
     __syncthreads();  // buffers are reused by the epilogue stage
 
