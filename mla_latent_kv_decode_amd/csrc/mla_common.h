@@ -132,16 +132,26 @@ MLA_DEV int64_t uniform64(int64_t v) {
   return int64_t((uint64_t(hi) << 32) | lo);
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP moves (six
+// VALU adds, no LDS round trips): shifts by 1, 2, 4 and 8 lanes within each
+// row of 16 (lanes without a source add 0), then lane 15 of rows 0 and 2 is
+// added to rows 1 and 3, and lane 31 to rows 2 and 3.
+MLA_DEV int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // Exclusive scan of one int per thread across the workgroup; returns the
 // thread's exclusive prefix and writes the total (wave-uniform) to *total.
 template <int NT>
 MLA_DEV int block_excl_scan(int v, int* red, int* total) {
   const int t = tid_fresh(), l = t % kWave, w = t / kWave;
-  int incl = v;
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(incl, o, 64);
-    if (l >= o) incl += t;
-  }
+  const int incl = wave_incl_scan(v);
   lds_barrier();
   if (l == kWave - 1) red[w] = incl;
   lds_barrier();
@@ -159,11 +169,7 @@ MLA_DEV int block_excl_scan(int v, int* red, int* total) {
 template <int NT>
 MLA_DEV int2 block_excl_scan2(int va, int vb, int* red, int* tota, int* totb) {
   const int t = tid_fresh(), l = t % kWave, w = t / kWave;
-  int ia = va, ib = vb;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int ta = __shfl_up(ia, o, 64), tb = __shfl_up(ib, o, 64);
-    if (l >= o) { ia += ta; ib += tb; }
-  }
+  const int ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
   lds_barrier();
   if (l == kWave - 1) { red[w] = ia; red[NT / kWave + w] = ib; }
   lds_barrier();
