@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense, published
 BYTES_PER_KV_TOKEN = {"bf16": 1152, "fp8": 596, "fp32": 2304}
 
 
@@ -59,6 +59,8 @@ def parse():
                         "mla_decode_combine_out_proj")
     p.add_argument("--graph", action="store_true",
                    help="capture each step (per pool copy) into one HIP graph and replay it")
+    p.add_argument("--no-calibration", action="store_true",
+                   help="skip the achievable-peak calibration (copy kernel, MFMA loop)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (5 times), to "
                         "scale HBM byte counters; prints nothing else")
@@ -118,6 +120,9 @@ def main():
     table, nblk = W.page_table(lens, bs, cfg.seed)
     kv_tokens = int(lens.sum())
     cdt = {"bf16": M.BF16, "fp8": M.FP8_E4M3}[cfg.cache_dtype]
+    # the arithmetic type of the decode's matrix products: both caches are
+    # multiplied on bf16 MFMA (the fp8 cache is dequantised to bf16 in LDS)
+    compute_dtype = "bf16"
     dims = M.make_dims(H, d.d_latent, d.d_rope, d.d_nope, d.d_v, bs, cdt, M.BF16,
                        flags=M.FLAG_GENERIC_DECODE if args.generic else 0)
 
@@ -187,6 +192,10 @@ def main():
     names = (["append", "query_absorb", "decode", "combine", "out_proj"] if args.separate
              else ["append_query_absorb", "decode", "combine_out_proj"])
 
+    # Achievable peaks on this chip (a plain device copy, a bf16 MFMA loop),
+    # measured first; they are reported beside the nominal peaks.
+    achievable = None if args.no_calibration else calibrate(M, stream)
+
     for i in range(args.warmup):
         for c in calls(i):
             c()
@@ -249,19 +258,29 @@ def main():
     decode_ms = float(k_ms[names.index("decode")])
 
     # ---- roofline of the dominant kernel (decode) ---------------------------
+    # t_roof = max(bytes / HBM peak, flops / MFMA peak of the arithmetic dtype):
+    # whichever is larger bounds the kernel and is the one reported.
     bytes_alg = kv_tokens * BYTES_PER_KV_TOKEN[cfg.cache_dtype] + B * n_q * H * D * 2
     flops_alg = kv_tokens * n_q * 2 * H * (D + d.d_latent)
     achieved_gbps = bytes_alg / (decode_ms * 1e-3) / 1e9
     achieved_tflops = flops_alg / (decode_ms * 1e-3) / 1e12
+    mfma_peak = MFMA_PEAK_TFLOPS[compute_dtype]
+    t_hbm = bytes_alg / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops_alg / (mfma_peak * 1e12)
     kernel_src = "decode_generic.hip" if args.generic else "decode_mfma.hip"
     traffic = traffic_from_profile(kernel_src, args.workload)
-    roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": traffic,
-                "mfma_tflops": round(achieved_tflops, 1),
-                "mfma_frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "bytes_alg_per_launch": bytes_alg, "flops_alg_per_launch": flops_alg,
-                "kernel_ms": round(decode_ms, 5)}
+    if t_hbm >= t_mfma:
+        roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": round(achieved_tflops / mfma_peak, 4)}
+    roofline.update({"traffic": traffic,
+                     "hbm_gbps": round(achieved_gbps, 1), "hbm_frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+                     "mfma_tflops": round(achieved_tflops, 1), "mfma_frac": round(achieved_tflops / mfma_peak, 4),
+                     "mfma_dtype": compute_dtype, "t_roof_ms": round(max(t_hbm, t_mfma) * 1e3, 5),
+                     "bytes_alg_per_launch": bytes_alg, "flops_alg_per_launch": flops_alg,
+                     "kernel_ms": round(decode_ms, 5), "achievable": achievable})
 
     # ---- the dense layers around the step (outside the timed region) -------
     dense = None if args.no_dense else dense_layers(M, W, dims, d, B * n_q, args.steps, stream)
@@ -279,11 +298,11 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": compute_dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={B} L={'ragged' if cfg.seq_len is None else cfg.seq_len} "
                                f"n_q={n_q} H={H} d_c={d.d_latent} d_R={d.d_rope} block={bs} "
                                f"cache={cfg.cache_dtype}",
-                   "batch": B, "kv_tokens_per_step": kv_tokens, "n_q": n_q,
+                   "batch": B, "kv_tokens_per_step": kv_tokens, "n_q": n_q, "cache_dtype": cfg.cache_dtype,
                    "partitions": G, "pool_copies_rotated": n_copies},
         "kernels_ms": {n: round(float(t), 5) for n, t in zip(names, k_ms)},
         "evented_step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 5),
@@ -292,6 +311,7 @@ def main():
         "decode_combine_kv_tokens_per_s": {"value": round(kv_tokens / (dc_ms * 1e-3), 1), "calls": dc},
         "decode_kernel": "generic" if args.generic else "default",
         "launch": "hip_graph_replay" if args.graph else "direct",
+        "calibration_before_timed_steps": achievable is not None,
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "dense_layers": dense,
@@ -336,11 +356,53 @@ def dense_layers(M, W, dims, d, rows, steps, stream):
     return out
 
 
-def cpu_baseline(cfg, pool, sc, table, lens, q_in, w_uk, h, w_dkv, w_kr, w_uv, seconds):
-    """The oracle as it stands (float64 NumPy), on a bounded sample of the same
-    workload: the first few sequences' append rows, query absorption, decode
-    and up-projection, repeated until about ``seconds`` of CPU work."""
+def calibrate(M, stream):
+    """Achievable peaks: a plain 1 GiB device-to-device copy (read + write bytes
+    per second) and a bf16 MFMA loop (libmla_calib.so, 2048 workgroups of
+    eight waves, four independent accumulators each), 10 launches each, median."""
+    import ctypes
     import torch
+    out = {}
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ts = []
+    for i in range(12):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1))
+    out["copy_gbps"] = round(2 * n / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+    del src, dst
+    calib = ctypes.CDLL(os.path.join(os.path.dirname(M.LIB_PATH), "libmla_calib.so"))
+    calib.mla_calib_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    wgs, iters = 2048, 256
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+    ts = []
+    for i in range(12):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert calib.mla_calib_mfma_loop(iters, wgs, sink.data_ptr(), stream.cuda_stream) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1))
+    flops = wgs * 8 * iters * 32 * 32768
+    out["mfma_loop_bf16_tflops"] = round(flops / (float(np.median(ts)) * 1e-3) / 1e12, 1)
+    out["note"] = "achievable on this chip: device copy (read+write) and a bf16 MFMA loop"
+    return out
+
+
+def cpu_baseline(cfg, pool, sc, table, lens, q_in, w_uk, h, w_dkv, w_kr, w_uv, seconds):
+    """The oracle as it stands, in float32 (its dtype argument; parity uses
+    float64), on a bounded sample of the same workload: the first few
+    sequences' append rows, query absorption, absorbed decode and W^UV.  Three
+    runs of about seconds/3 each; the median run's rate is reported."""
+    import torch
+    from threadpoolctl import threadpool_info
     from oracle import mla_oracle as O
 
     d = cfg.dims
@@ -360,32 +422,43 @@ def cpu_baseline(cfg, pool, sc, table, lens, q_in, w_uk, h, w_dkv, w_kr, w_uv, s
         s[blocks] = sc.index_select(0, idx).cpu().numpy()
         host_pool["scales"] = s
 
-    def f64(t):
-        return O.bf16_bits_to_f64(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+    def f32(t):
+        return O.bf16_bits_to_f64(t.detach().cpu().view(torch.int16).numpy().view(np.uint16)).astype(np.float32)
 
-    qin = f64(q_in[:n_seq])
-    hh = f64(h[:n_seq * cfg.n_q])
-    wd, wk, wu, wq = f64(w_dkv), f64(w_kr), f64(w_uv), f64(w_uk)
+    qin = f32(q_in[:n_seq])
+    hh = f32(h[:n_seq * cfg.n_q])
+    wd, wk, wu, wq = f32(w_dkv), f32(w_kr), f32(w_uv), f32(w_uk)
     scale = O.softmax_scale(d.d_nope, d.d_rope)
     pos = (lens[:n_seq].repeat(cfg.n_q) - 1).astype(np.int64)
     qpos = (lens[:n_seq, None] - cfg.n_q + np.arange(cfg.n_q)[None, :]).astype(np.int64)
-    reps, t_start = 0, time.perf_counter()
-    while True:
-        O.kv_rows(hh, wd, wk, pos)
-        qh = O.absorb_query(qin[..., :d.d_nope], qin[..., d.d_nope:], wq, qpos)
-        res = O.decode(qh, host_pool, table, lens, bs, d.d_latent, scale, batch_ids=ids)
-        O.out_proj(np.concatenate([res[b][0] for b in ids]), wu)
-        reps += 1
-        el = time.perf_counter() - t_start
-        if el >= seconds or reps >= 1000:
-            break
-    cores = len(os.sched_getaffinity(0))
-    return {"value": round(reps * int(lens[:n_seq].sum()) / el, 1), "unit": "KV-tokens/s",
-            "cores": cores, "kind": "oracle",
+    f = np.float32
+
+    def one_rep():
+        O.kv_rows(hh, wd, wk, pos, dtype=f)
+        qh = O.absorb_query(qin[..., :d.d_nope], qin[..., d.d_nope:], wq, qpos, dtype=f)
+        res = O.decode(qh, host_pool, table, lens, bs, d.d_latent, scale, batch_ids=ids, dtype=f)
+        O.out_proj(np.concatenate([res[b][0] for b in ids]), wu, dtype=f)
+
+    rates, reps_all = [], []
+    for run in range(3):
+        reps, t_start = 0, time.perf_counter()
+        while True:
+            one_rep()
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el >= seconds / 3 or reps >= 1000:
+                break
+        rates.append(reps * int(lens[:n_seq].sum()) / el)
+        reps_all.append(reps)
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = blas[0]["num_threads"] if blas else len(os.sched_getaffinity(0))
+    lib = f"{blas[0].get('internal_api', '?')} {blas[0].get('version', '')}".strip() if blas else "unknown"
+    return {"value": round(float(np.median(rates)), 1), "unit": "KV-tokens/s",
+            "cores": threads, "kind": "oracle", "blas": lib,
+            "runs": [round(r, 1) for r in rates],
             "sample": f"{n_seq} of {cfg.batch} sequences ({int(lens[:n_seq].sum())} KV-tokens), "
-                      f"append rows + query absorption + absorbed decode + W^UV in float64 NumPy, "
-                      f"{reps} repetitions "
-                      f"in {el:.1f} s"}
+                      f"append rows + query absorption + absorbed decode + W^UV in float32 NumPy "
+                      f"({lib}, {threads} threads); median of 3 runs of {reps_all} repetitions"}
 
 
 if __name__ == "__main__":

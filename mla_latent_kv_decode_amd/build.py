@@ -1,7 +1,9 @@
 """Build the HIP library ``libmla.so`` for gfx950, in-tree.
 
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
-parallel) and linked into ``mla_latent_kv_decode_amd/libmla.so``.  hipcc
+parallel) and linked into ``mla_latent_kv_decode_amd/libmla.so``; the
+benchmark's calibration kernel (``calib/peak.hip``) goes into
+``libmla_calib.so`` beside it.  hipcc
 cross-compiles for gfx950 without a GPU present.
 """
 from __future__ import annotations
@@ -18,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
+CALIB_LIB = os.path.join(PKG, "libmla_calib.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -52,6 +55,16 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    # the benchmark's achievable-peak calibration (not part of the ABI)
+    cobj = _compile(os.path.join(PKG, "calib", "peak.hip"))
+    ctmp = CALIB_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", cobj, "-o", ctmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(ctmp, CALIB_LIB)
+    if verbose:
+        print(f"built {CALIB_LIB}")
     return LIB
 
 

@@ -8,7 +8,10 @@ the product path.
 Everything is computed in float64 from inputs that are upcast exactly from
 the stored values (fp32, bf16 bit patterns, or e4m3 codes times fp32 scales).
 The arithmetic is the plain definition, step by step, with no blocking,
-fusion or reordering.
+fusion or reordering.  The functions the benchmark's CPU baseline runs
+(``kv_rows``, ``absorb_query``, ``decode`` / ``attend_absorbed``,
+``out_proj``) take a ``dtype`` argument so that the same steps can be timed
+in float32; every parity test uses the float64 default.
 
 Sources (page titles; sections named on each page):
 
@@ -184,15 +187,15 @@ def rope(x, pos, base: float = 10000.0) -> np.ndarray:
 # cache append ([MLA-93] Core Mechanics 1 and 3; decoding section)
 # --------------------------------------------------------------------------
 
-def kv_rows(h, w_dkv, w_kr, positions, base: float = 10000.0) -> np.ndarray:
+def kv_rows(h, w_dkv, w_kr, positions, base: float = 10000.0, dtype=np.float64) -> np.ndarray:
     """Cached rows [c ; k^R] for hidden states h [T, d_model].
 
     c = W^DKV h (W^DKV: [d_c, d_model]); k^R = RoPE(W^KR h, pos)
-    (W^KR: [d_R, d_model]).  Returns float64 [T, d_c + d_R].
+    (W^KR: [d_R, d_model]).  Returns [T, d_c + d_R] (float64 by default).
     """
-    h = np.asarray(h, dtype=np.float64)
-    c = h @ np.asarray(w_dkv, dtype=np.float64).T
-    kr = rope(h @ np.asarray(w_kr, dtype=np.float64).T, np.asarray(positions), base)
+    h = np.asarray(h, dtype=dtype)
+    c = h @ np.asarray(w_dkv, dtype=dtype).T
+    kr = rope(h @ np.asarray(w_kr, dtype=dtype).T, np.asarray(positions), base).astype(dtype)
     return np.concatenate([c, kr], axis=-1)
 
 
@@ -265,24 +268,24 @@ def visible(seq_len: int, n_q: int, j: int) -> int:
     return seq_len - n_q + j + 1
 
 
-def attend_absorbed(q_b, rows, n_q: int, d_latent: int, scale: float):
+def attend_absorbed(q_b, rows, n_q: int, d_latent: int, scale: float, dtype=np.float64):
     """Absorbed-form attention for one sequence.
 
     q_b: [n_q, H, d_c + d_R] packed [q~ ; q^R]; rows: [L, d_c + d_R] cached
     [c ; k^R].  Score s_t = scale * (q~ . c_t + q^R . k^R_t); p = softmax over
     the visible positions; u = sum_t p_t c_t ([MLA-93] Core Mechanics 3, the
     absorbed query and latent value aggregation).
-    Returns u [n_q, H, d_c] and lse [n_q, H] (natural log), float64.
+    Returns u [n_q, H, d_c] and lse [n_q, H] (natural log), float64 by default.
     """
-    q_b = np.asarray(q_b, dtype=np.float64)
-    rows = np.asarray(rows, dtype=np.float64)
+    q_b = np.asarray(q_b, dtype=dtype)
+    rows = np.asarray(rows, dtype=dtype)
     L = rows.shape[0]
     n_heads = q_b.shape[1]
-    u = np.zeros((n_q, n_heads, d_latent))
-    lse = np.zeros((n_q, n_heads))
+    u = np.zeros((n_q, n_heads, d_latent), dtype=dtype)
+    lse = np.zeros((n_q, n_heads), dtype=dtype)
     for j in range(n_q):
         n = visible(L, n_q, j)
-        s = scale * (q_b[j] @ rows[:n].T)                  # [H, n]
+        s = dtype(scale) * (q_b[j] @ rows[:n].T)           # [H, n]
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         z = e.sum(axis=1, keepdims=True)
@@ -292,7 +295,7 @@ def attend_absorbed(q_b, rows, n_q: int, d_latent: int, scale: float):
 
 
 def decode(q, pool: dict, page_table, seq_lens, block_size: int, d_latent: int,
-           scale: float, batch_ids: Iterable[int] = None):
+           scale: float, batch_ids: Iterable[int] = None, dtype=np.float64):
     """Absorbed decode of a batch (or of the listed sequences).
 
     q: [B, n_q, H, D].  Returns dict b -> (u [n_q, H, d_c], lse [n_q, H]).
@@ -303,7 +306,7 @@ def decode(q, pool: dict, page_table, seq_lens, block_size: int, d_latent: int,
     ids = range(q.shape[0]) if batch_ids is None else batch_ids
     for b in ids:
         rows = gather_sequence(pool, page_table, b, int(seq_lens[b]), block_size)
-        out[b] = attend_absorbed(q[b], rows, n_q, d_latent, scale)
+        out[b] = attend_absorbed(q[b], rows, n_q, d_latent, scale, dtype)
     return out
 
 
@@ -408,10 +411,10 @@ def combine(o_parts, lse_parts):
 # per-head value up-projection ([MLA-93] decoding section)
 # --------------------------------------------------------------------------
 
-def out_proj(u, w_uv) -> np.ndarray:
+def out_proj(u, w_uv, dtype=np.float64) -> np.ndarray:
     """o[r, i, :] = W^UV_i u[r, i, :] with W^UV: [H, d_v, d_c]."""
-    u = np.asarray(u, dtype=np.float64)
-    w = np.asarray(w_uv, dtype=np.float64)
+    u = np.asarray(u, dtype=dtype)
+    w = np.asarray(w_uv, dtype=dtype)
     return np.einsum("rid,ivd->riv", u, w)
 
 
@@ -426,18 +429,18 @@ def split_query(qfull, n_heads: int, d_nope: int, d_rope: int):
     return q[..., :d_nope], q[..., d_nope:]
 
 
-def absorb_query(q_c, q_r, w_uk, pos, base: float = 10000.0):
+def absorb_query(q_c, q_r, w_uk, pos, base: float = 10000.0, dtype=np.float64):
     """Packed absorbed query [q~ ; RoPE(q^R, pos)].
 
     q~_i = (W^UK_i)^T q^C_i in R^{d_c}: the associativity regrouping of
     Core Mechanics 3.  q_c: [.., H, d_nope]; q_r: [.., H, d_R];
     w_uk: [H, d_nope, d_c]; pos broadcasts against the leading axes.
     """
-    q_c = np.asarray(q_c, dtype=np.float64)
-    w = np.asarray(w_uk, dtype=np.float64)
+    q_c = np.asarray(q_c, dtype=dtype)
+    w = np.asarray(w_uk, dtype=dtype)
     q_t = np.einsum("...in,inc->...ic", q_c, w)
     pos = np.asarray(pos, dtype=np.float64)
-    q_rr = rope(q_r, pos[..., None] if pos.ndim else pos, base)
+    q_rr = rope(q_r, pos[..., None] if pos.ndim else pos, base).astype(dtype)
     return np.concatenate([q_t, q_rr], axis=-1)
 
 
