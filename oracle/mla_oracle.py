@@ -341,6 +341,27 @@ def attend_unabsorbed(q_c, q_r, rows, w_uk, w_uv, n_q: int, d_latent: int, scale
     return o
 
 
+def prefill_chunk(q_in, rows, w_uk, w_uv, d_latent: int, d_nope: int, scale: float,
+                  base: float = 10000.0):
+    """A prefill chunk over the latent cache in the un-absorbed form.
+
+    The prefill phase processes many prompt tokens at once ([MLA-93], the
+    prefill/decode contrast at its start); for a long chunk the per-head keys
+    and values are expanded from the cached latents once (k = [W^UK_i c ; k^R],
+    v = W^UV_i c) and attention runs in the usual form.  q_in: [C, H, d_nope +
+    d_R] per head q^C and the not yet rotated q^R of the chunk's C tokens;
+    rows: [T, D] the cached rows of the sequence, the chunk's own C rows last
+    (chunk token i sits at position T - C + i and sees positions 0 .. T - C + i).
+    q^R is rotated at each token's position.  Returns o [C, H, d_v].
+    """
+    q_in = np.asarray(q_in, dtype=np.float64)
+    C = q_in.shape[0]
+    T = np.asarray(rows).shape[0]
+    pos = np.arange(T - C, T, dtype=np.float64)
+    q_r = rope(q_in[..., d_nope:], pos[:, None], base)
+    return attend_unabsorbed(q_in[..., :d_nope], q_r, rows, w_uk, w_uv, C, d_latent, scale)
+
+
 def attend_bruteforce(q_b, rows, n_q: int, d_latent: int, scale: float):
     """Explicit loops, softmax as exp(s) / sum exp(s) with no max shift.
 

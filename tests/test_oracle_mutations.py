@@ -110,7 +110,30 @@ def _absorb_first_row_position(q_c, q_r, w_uk, pos, base=10000.0):
     return _orig_absorb_query(q_c, q_r, w_uk, np.full_like(p, p.flat[0]) if p.ndim else p, base)
 
 
+def _prefill_positions_from_zero(q_in, rows, w_uk, w_uv, d_latent, d_nope, scale, base=10000.0):
+    # q^R rotated at 0 .. C-1 instead of the tokens' own positions
+    q_in = np.asarray(q_in, dtype=np.float64)
+    C = q_in.shape[0]
+    q_r = O.rope(q_in[..., d_nope:], np.arange(C, dtype=np.float64)[:, None], base)
+    return O.attend_unabsorbed(q_in[..., :d_nope], q_r, rows, w_uk, w_uv, C, d_latent, scale)
+
+
+def _prefill_not_causal(q_in, rows, w_uk, w_uv, d_latent, d_nope, scale, base=10000.0):
+    # every chunk token sees the whole chunk
+    q_in = np.asarray(q_in, dtype=np.float64)
+    C, T = q_in.shape[0], np.asarray(rows).shape[0]
+    pos = np.arange(T - C, T, dtype=np.float64)
+    q_r = O.rope(q_in[..., d_nope:], pos[:, None], base)
+    return np.concatenate([O.attend_unabsorbed(q_in[i:i + 1, :, :d_nope], q_r[i:i + 1], rows, w_uk, w_uv, 1,
+                                               d_latent, scale) for i in range(C)])
+
+
 MUTANTS = {
+    "prefill_rope_positions_from_zero": ("prefill_chunk", _prefill_positions_from_zero,
+                                         [P.test_prefill_chunk_equals_absorbed_decode_of_every_token]),
+    "prefill_not_causal": ("prefill_chunk", _prefill_not_causal,
+                           [P.test_prefill_chunk_equals_absorbed_decode_of_every_token,
+                            P.test_prefill_chunk_split_in_two_gives_the_same_outputs]),
     "fp8_dequant_tile0_scale": ("dequantize_fp8_rows", _dequant_tile0_scale,
                                 [P.test_dequantize_fp8_rows_per_tile_scales]),
     "fp8_dequant_tiles_of_64": ("dequantize_fp8_rows", _dequant_tiles_of_64,

@@ -533,3 +533,44 @@ def test_absorbed_query_rope_half_is_rotated_at_each_rows_position():
             R = np.array([[math.cos(th), -math.sin(th)], [math.sin(th), math.cos(th)]])
             for i in range(H):
                 np.testing.assert_allclose(packed[b, j, i, d_c:], R @ q_r[b, j, i], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# chunked prefill (un-absorbed form over the latent cache)
+# --------------------------------------------------------------------------
+def test_prefill_chunk_equals_absorbed_decode_of_every_token():
+    """The un-absorbed chunk equals, token by token, the absorbed decode of
+    that token at its own position followed by W^UV (associativity, [MLA-93]
+    Core Mechanics 3), with the causal rule of the decode (each token sees the
+    cache up to and including itself)."""
+    rng = np.random.default_rng(120)
+    H, d_c, d_r, d_nope, d_v, T, C = 3, 8, 4, 5, 6, 11, 4
+    rows = rng.standard_normal((T, d_c + d_r))
+    q_in = rng.standard_normal((C, H, d_nope + d_r))
+    w_uk = rng.standard_normal((H, d_nope, d_c)) / math.sqrt(d_c)
+    w_uv = rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c)
+    scale = O.softmax_scale(d_nope, d_r)
+    o = O.prefill_chunk(q_in, rows, w_uk, w_uv, d_c, d_nope, scale)
+    assert o.shape == (C, H, d_v)
+    for i in range(C):
+        p = T - C + i
+        q = O.absorb_query(q_in[i:i + 1, :, :d_nope], q_in[i:i + 1, :, d_nope:], w_uk, np.array([p]))
+        u, _ = O.attend_absorbed(q, rows[:p + 1], 1, d_c, scale)
+        np.testing.assert_allclose(o[i], O.out_proj(u, w_uv)[0], rtol=1e-11, atol=1e-12)
+
+
+def test_prefill_chunk_split_in_two_gives_the_same_outputs():
+    """A prompt processed as one chunk or as two consecutive chunks (the
+    second seeing the first through the cache) gives every token the same
+    output: chunking changes the schedule, not the attention."""
+    rng = np.random.default_rng(121)
+    H, d_c, d_r, d_nope, d_v, T0, C = 2, 8, 4, 5, 6, 7, 6
+    rows = rng.standard_normal((T0 + C, d_c + d_r))
+    q_in = rng.standard_normal((C, H, d_nope + d_r))
+    w_uk = rng.standard_normal((H, d_nope, d_c)) / math.sqrt(d_c)
+    w_uv = rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c)
+    scale = O.softmax_scale(d_nope, d_r)
+    whole = O.prefill_chunk(q_in, rows, w_uk, w_uv, d_c, d_nope, scale)
+    first = O.prefill_chunk(q_in[:2], rows[:T0 + 2], w_uk, w_uv, d_c, d_nope, scale)
+    second = O.prefill_chunk(q_in[2:], rows, w_uk, w_uv, d_c, d_nope, scale)
+    np.testing.assert_allclose(np.concatenate([first, second]), whole, rtol=1e-12, atol=1e-13)
