@@ -297,6 +297,43 @@ int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
                                 mla_stream_t stream);
 
 /*
+ * mla_prefill -- one prefill chunk of a sequence over its latent cache, in
+ * the un-absorbed form.  The prefill phase processes many prompt tokens at
+ * once ([MLA-93], the prefill/decode contrast that opens the page); for a
+ * long chunk the per-head keys and values are expanded from the cached
+ * latents once per chunk (k_{t,i} = [W^UK_i c_t ; k^R_t], v_{t,i} = W^UV_i c_t,
+ * [MLA-93] Core Mechanics 1 and 3) and attention runs in the usual form.
+ * The chunk's own rows must already be in the cache (mla_cache_append): chunk
+ * token j sits at position seq_len - n_tokens + j and attends to positions
+ * 0 .. seq_len - n_tokens + j.  Per head i:
+ *   o_i = sum_t softmax_t(scale * [q^C_i ; RoPE(q^R_i)] . k_{t,i}) v_{t,i}
+ * (the rotation of q^R at the token's position is done here).
+ *   q_in           [n_tokens][num_heads][d_nope + d_rope] bf16: per head q^C
+ *                  then the not yet rotated q^R (mla_query_absorb's input layout)
+ *   cache          the paged pool (bf16); page_table_row [>= ceil(seq_len /
+ *                  block_size)] int32: the sequence's row of the page table
+ *   w_uk           [num_heads][d_nope][d_latent] bf16; w_uv [num_heads][d_v][d_latent]
+ *   out            [n_tokens][num_heads][d_v] bf16 (the heads' outputs before W^O)
+ *   workspace      mla_prefill_workspace_size(dims, n_tokens, seq_len) bytes,
+ *                  256-byte aligned: the gathered latents and the expanded keys
+ *                  and values ((d_latent + d_rope + 2 * 128 * num_heads) * 2
+ *                  bytes per cached token) plus scratch
+ * Supported: bf16 activations and cache with the DeepSeek-V3 dimensions
+ * (H = 128, d_latent = 512, d_rope = 64, d_nope = d_v = 128); other dims
+ * return MLA_ERR_UNSUPPORTED (the workspace size is 0).  fp32 accumulation,
+ * RoPE angles in fp64 with cos/sin rounded to fp32, bf16 outputs.
+ * Errors: MLA_ERR_INVALID_ARGUMENT (n_tokens < 0, seq_len < n_tokens, NULL or
+ * misaligned pointers: q, cache and weights 16 bytes, out 8),
+ * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_UNSUPPORTED.  n_tokens = 0 does
+ * nothing.
+ */
+size_t mla_prefill_workspace_size(const mla_dims *dims, int32_t n_tokens, int32_t seq_len);
+
+int mla_prefill(const mla_dims *dims, const void *q_in, int32_t n_tokens, const void *cache,
+                const int32_t *page_table_row, int32_t seq_len, const void *w_uk, const void *w_uv,
+                void *out, void *workspace, size_t workspace_bytes, mla_stream_t stream);
+
+/*
  * mla_decode_noalloc -- mla_decode followed by mla_decode_combine, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc).  Instead of a

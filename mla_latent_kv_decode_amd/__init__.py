@@ -11,4 +11,5 @@ from ._lib import (  # noqa: F401
     mla_device_cu_count, mla_dims, mla_linear, mla_linear_workspace_size, mla_out_proj,
     mla_query_absorb,
     mla_cache_append_query_absorb, mla_decode_noalloc, NOALLOC_SCRATCH_BYTES,
+    mla_prefill, mla_prefill_workspace_size,
 )

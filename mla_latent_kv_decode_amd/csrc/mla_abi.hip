@@ -2,6 +2,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstdlib>
 #include <map>
 #include <mutex>
@@ -598,6 +599,104 @@ int mla_decode_combine_out_proj(const mla_dims* d, const void* workspace, size_t
                                  num_partitions, u_out, lse_out, stream))
     return r;
   return mla_out_proj(d, u_out, batch * n_q, w_uv, out, stream);
+}
+
+namespace {
+// Prefill workspace: gathered latents c [T][d_c] and RoPE keys [T][d_R], the
+// expanded content keys and values [T][H * d_nope], [T][H * d_v] (act dtype),
+// then the expansion's linear-layer scratch.
+struct PrefillLayout {
+  size_t kr_off, kc_off, v_off, q_off, lin_off, lin_bytes, total;
+};
+PrefillLayout prefill_layout(const mla_dims* d, int n_tokens, int seq_len) {
+  PrefillLayout w;
+  const size_t T = size_t(seq_len), e = 2;
+  w.kr_off = align_up(T * d->d_latent * e, 256);
+  w.kc_off = align_up(w.kr_off + T * d->d_rope * e, 256);
+  w.v_off = align_up(w.kc_off + T * size_t(d->num_heads) * d->d_nope * e, 256);
+  w.q_off = align_up(w.v_off + T * size_t(d->num_heads) * d->d_v * e, 256);
+  w.lin_off = align_up(w.q_off + size_t(n_tokens) * d->num_heads * (d->d_nope + d->d_rope) * e, 256);
+  mla::LinearArgs la{};
+  la.rows = seq_len;
+  la.k = d->d_latent;
+  la.act_dtype = MLA_BF16;
+  la.n = d->num_heads * d->d_nope;
+  size_t lin = mla::linear_mfma_workspace(la);
+  la.n = d->num_heads * d->d_v;
+  lin = std::max(lin, mla::linear_mfma_workspace(la));
+  w.lin_bytes = lin;
+  w.total = align_up(w.lin_off + lin, 256);
+  return w;
+}
+bool prefill_dims_ok(const mla_dims* d) {
+  return d->act_dtype == MLA_BF16 && d->cache_dtype == MLA_BF16 && d->num_heads == 128 && d->d_latent == 512 &&
+         d->d_rope == 64 && d->d_nope == 128 && d->d_v == 128;
+}
+}  // namespace
+
+size_t mla_prefill_workspace_size(const mla_dims* d, int32_t n_tokens, int32_t seq_len) {
+  if (!d || n_tokens < 1 || seq_len < n_tokens || !prefill_dims_ok(d)) return 0;
+  return prefill_layout(d, n_tokens, seq_len).total;
+}
+
+int mla_prefill(const mla_dims* d, const void* q_in, int32_t n_tokens, const void* cache,
+                const int32_t* page_table_row, int32_t seq_len, const void* w_uk, const void* w_uv, void* out,
+                void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+  if (int e = check_dims(d, true)) return e;
+  if (n_tokens < 0 || seq_len < n_tokens)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "n_tokens=%d seq_len=%d (need 0 <= n_tokens <= seq_len)", n_tokens,
+                seq_len);
+  if (n_tokens == 0) return ok();
+  if (!prefill_dims_ok(d))
+    return fail(MLA_ERR_UNSUPPORTED, "prefill: bf16 activations and cache with H=128, d_latent=512, d_rope=64, "
+                                     "d_nope=128, d_v=128 only");
+  if (!q_in || !cache || !page_table_row || !w_uk || !w_uv || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q_in, 16) || !aligned(cache, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) || !aligned(out, 8) ||
+      !aligned(page_table_row, 4) || !aligned(workspace, 256))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer (q, cache, weights 16 B; out 8 B; workspace 256 B)");
+  const PrefillLayout w = prefill_layout(d, n_tokens, seq_len);
+  if (workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "prefill workspace %zu bytes < %zu required", workspace_bytes, w.total);
+  char* ws = static_cast<char*>(workspace);
+  mla::PrefillArgs a;
+  a.q = q_in;
+  a.cache = cache;
+  a.page_table = page_table_row;
+  a.ws_c = ws;
+  a.ws_kr = ws + w.kr_off;
+  a.ws_kc = ws + w.kc_off;
+  a.ws_v = ws + w.v_off;
+  a.ws_q = ws + w.q_off;
+  a.out = out;
+  a.n_tokens = n_tokens;
+  a.seq_len = seq_len;
+  a.block_size = d->block_size;
+  a.H = d->num_heads;
+  a.d_latent = d->d_latent;
+  a.d_rope = d->d_rope;
+  a.d_nope = d->d_nope;
+  a.d_v = d->d_v;
+  a.scale = eff_scale(d);
+  a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  if (!mla::prefill_supported(a)) return fail(MLA_ERR_INVALID_ARGUMENT, "prefill: misaligned pointer");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_prefill_gather(a, st);
+  // the expansion: K^C = c W^UK^T and V = c W^UV^T (W^UK, W^UV: [H][128][d_c] = [H*128][d_c])
+  for (int m = 0; m < 2 && e == hipSuccess; ++m) {
+    mla::LinearArgs la{};
+    la.x = a.ws_c;
+    la.w = m == 0 ? w_uk : w_uv;
+    la.y = ws + (m == 0 ? w.kc_off : w.v_off);
+    la.rows = seq_len;
+    la.n = d->num_heads * (m == 0 ? d->d_nope : d->d_v);
+    la.k = d->d_latent;
+    la.act_dtype = MLA_BF16;
+    e = mla::launch_linear_mfma(la, ws + w.lin_off, st);
+  }
+  if (e == hipSuccess) e = mla::launch_prefill_attn(a, st);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
 }
 
 int mla_decode_noalloc(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, const void* cache,

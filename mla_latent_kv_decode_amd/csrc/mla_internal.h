@@ -109,6 +109,25 @@ struct OutProjArgs {
   int act_dtype;
 };
 
+// chunked prefill (un-absorbed form): gather, then expansion by two linear
+// layers, then attention
+struct PrefillArgs {
+  const void* q;             // [C][H][d_nope + d_rope] bf16, q^R not yet rotated
+  const void* cache;         // paged pool [nblk][bs][D] bf16
+  const int32_t* page_table; // the sequence's row
+  void* ws_c;                // [T][d_latent] gathered latents
+  void* ws_kr;               // [T][d_rope] gathered RoPE keys
+  const void* ws_kc;         // [T][H * d_nope] expanded content keys
+  const void* ws_v;          // [T][H * d_v] expanded values
+  void* ws_q;                // [C][H][d_nope + d_rope] the queries, q^R rotated
+  void* out;                 // [C][H][d_v] bf16
+  int n_tokens, seq_len, block_size, H, d_latent, d_rope, d_nope, d_v;
+  float scale, rope_base;
+};
+bool prefill_supported(const PrefillArgs& a);
+hipError_t launch_prefill_gather(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t st);
+
 bool decode_generic_supported(const DecodeArgs& a);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 bool decode_mfma_supported(const DecodeArgs& a);
