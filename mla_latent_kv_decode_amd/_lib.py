@@ -102,7 +102,7 @@ def lib():
         L.mla_prefill.argtypes = [D, _P, _I, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]
         for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj",
                   "mla_decode_combine_out_proj", "mla_query_absorb", "mla_cache_append_query_absorb",
-                  "mla_linear", "mla_decode_noalloc", "mla_prefill_workspace_size", "mla_prefill"):
+                  "mla_linear", "mla_decode_noalloc", "mla_prefill"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -125,8 +125,32 @@ def quantize_fp8_row(row) -> Tuple[np.ndarray, np.ndarray]:
     return codes, scales
 
 
-def quantize_fp8_rows(rows) -> Tuple[np.ndarray, np.ndarray]:
-    """``quantize_fp8_row`` applied to every row of [N, D] (vectorised over N)."""
+def pow2_scale_exponent(a: float) -> int:
+    """The smallest integer E with a <= 448 * 2^E, for a > 0.
+
+    A power-of-two tile scale 2^E maps the tile's largest magnitude a into
+    (224, 448]: the top binade of e4m3.  The pages ask for a scaling factor
+    per tile ([DUALPIPE] FP8 paragraph) without fixing its number format; a
+    power of two is the reading under which the scale can be applied by
+    exponent arithmetic alone.  The comparisons below are exact in float64.
+    """
+    a = float(a)
+    e = math.ceil(math.log2(a / E4M3_MAX))
+    while a > E4M3_MAX * 2.0 ** e:
+        e += 1
+    while a <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return e
+
+
+def quantize_fp8_rows(rows, pow2_scales: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """``quantize_fp8_row`` applied to every row of [N, D] (vectorised over N).
+
+    With ``pow2_scales`` each nonzero tile's scale is 2^E with
+    E = ``pow2_scale_exponent(a)`` (a = the tile's max |r|) and code =
+    e4m3(r * 2^-E), an exact fp32 scaling; zero tiles keep scale 1 and zero
+    codes.  The stored scale is still one fp32 value per (token, tile).
+    """
     r = np.asarray(rows, dtype=np.float32)
     tiles = fp8_tiles(r.shape[-1])
     codes = np.zeros(r.shape, dtype=np.uint8)
@@ -135,12 +159,38 @@ def quantize_fp8_rows(rows) -> Tuple[np.ndarray, np.ndarray]:
         a = np.max(np.abs(r[..., lo:hi]), axis=-1).astype(np.float32)
         nz = a != 0
         safe = np.where(nz, a, np.float32(1)).astype(np.float32)
-        inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
-        scales[..., k] = np.where(nz, (safe / np.float32(E4M3_MAX)).astype(np.float32),
-                                  np.float32(1))
+        if pow2_scales:
+            ex = np.array([pow2_scale_exponent(v) for v in safe.reshape(-1)], dtype=np.float64)
+            sc = np.exp2(ex).reshape(safe.shape).astype(np.float32)
+            inv = (np.float32(1) / sc).astype(np.float32)  # exact: a power of two
+            scales[..., k] = np.where(nz, sc, np.float32(1))
+        else:
+            inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
+            scales[..., k] = np.where(nz, (safe / np.float32(E4M3_MAX)).astype(np.float32),
+                                      np.float32(1))
         x = (r[..., lo:hi] * inv[..., None]).astype(np.float32)
         codes[..., lo:hi] = np.where(nz[..., None], e4m3_encode(x), np.uint8(0))
     return codes, scales
+
+
+def quantize_rows_e4m3_pow2(x) -> np.ndarray:
+    """Each row of x (last axis) rounded to e4m3 under one power-of-two scale.
+
+    The value an fp8 product sees for a query quantised with one scale per
+    head: scale 2^E with E = ``pow2_scale_exponent(max |row|)``, value =
+    e4m3(row * 2^-E) * 2^E (all-zero rows stay zero).  Returns float64 values.
+    """
+    r = np.asarray(x, dtype=np.float32)
+    flat = r.reshape(-1, r.shape[-1])
+    out = np.zeros(flat.shape, dtype=np.float64)
+    for i, row in enumerate(flat):
+        a = float(np.max(np.abs(row)))
+        if a == 0:
+            continue
+        e = pow2_scale_exponent(a)
+        codes = e4m3_encode((row * np.float32(2.0 ** -e)).astype(np.float32))
+        out[i] = e4m3_decode(codes) * 2.0 ** e
+    return out.reshape(r.shape)
 
 
 def dequantize_fp8_rows(codes, scales) -> np.ndarray:

@@ -46,6 +46,16 @@ def _rope_freq(x, pos, base=10000.0):
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], -1)
 
 
+_orig_pow2_exp = O.pow2_scale_exponent
+_orig_qrows = O.quantize_fp8_rows
+
+
+def _query_quant_shared_scale(x):
+    r = np.asarray(x, dtype=np.float32)
+    e = _orig_pow2_exp(float(np.max(np.abs(r))))
+    return O.e4m3_decode(O.e4m3_encode((r * np.float32(2.0 ** -e)).astype(np.float32))) * 2.0 ** e
+
+
 _orig_absorbed = O.attend_absorbed
 
 
@@ -169,6 +179,15 @@ MUTANTS = {
     "fp8_no_saturation": ("e4m3_encode", _encode_no_saturation,
                           [P.test_e4m3_encode_round_trip_ties_and_saturation]),
     "fp8_scale_off": ("E4M3_MAX", 447.0, [P.test_fp8_row_quantizer_properties]),
+    "pow2_exponent_floor": ("pow2_scale_exponent", lambda a: math.floor(math.log2(float(a) / 448.0)),
+                            [P.test_pow2_scale_exponent_brute_force_and_boundaries,
+                             P.test_fp8_pow2_quantizer_properties]),
+    "pow2_exponent_one_high": ("pow2_scale_exponent", lambda a: _orig_pow2_exp(a) + 1,
+                               [P.test_fp8_pow2_quantizer_properties, P.test_query_rows_e4m3_pow2]),
+    "pow2_scales_ignored": ("quantize_fp8_rows", lambda rows, pow2_scales=False: _orig_qrows(rows),
+                            [P.test_fp8_pow2_quantizer_properties]),
+    "query_quant_one_scale_for_all_rows": ("quantize_rows_e4m3_pow2", _query_quant_shared_scale,
+                                           [P.test_query_rows_e4m3_pow2]),
     "bf16_truncation": ("to_bf16_bits",
                         lambda x: (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16),
                         [P.test_bf16_rounding_known_values]),

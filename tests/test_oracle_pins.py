@@ -188,6 +188,79 @@ def test_fp8_row_quantizer_properties():
         assert np.array_equal(vc[r], c1) and np.array_equal(vs[r], s1)
 
 
+def _smallest_pow2_exponent(a):
+    """Brute force over exponents: the smallest E with a <= 448 * 2^E."""
+    return min(e for e in range(-160, 160) if a <= 448.0 * 2.0 ** e)
+
+
+def test_pow2_scale_exponent_brute_force_and_boundaries():
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([np.abs(rng.standard_normal(200)) * 10.0 ** rng.integers(-12, 12, 200),
+                           [448.0, 224.0, 56.0, 1.0, 2.0 ** -20, 3.5]])
+    for a in vals:
+        assert O.pow2_scale_exponent(a) == _smallest_pow2_exponent(a), a
+    # the tile maximum lands in the top binade (224, 448]
+    assert O.pow2_scale_exponent(448.0) == 0
+    assert O.pow2_scale_exponent(np.nextafter(448.0, 1e9)) == 1
+    assert O.pow2_scale_exponent(224.0) == -1
+    assert O.pow2_scale_exponent(np.nextafter(224.0, 1e9)) == 0
+
+
+def test_fp8_pow2_quantizer_properties():
+    """Power-of-two tile scales: each scale is 2^E with the tile maximum in
+    (224, 448] after scaling, and each code is the nearest e4m3 value (ties to
+    even) of r / scale, found by brute force over the code table."""
+    rng = np.random.default_rng(12)
+    rows = rng.standard_normal((6, 576)).astype(np.float32)
+    rows[:, [5, 300, 530]] *= 20
+    rows[1, 128:256] = 0.0                      # a zero tile
+    rows[2, 0:128] = rows[2, 0:128] / np.max(np.abs(rows[2, 0:128])) * 56.0   # amax = 448 * 2^-3
+    rows[3, 256:384] *= np.float32(1e-3)
+    codes, scales = O.quantize_fp8_rows(rows, pow2_scales=True)
+    assert codes.shape == rows.shape and scales.shape == (6, 5)
+    for r in range(6):
+        for k, (lo, hi) in enumerate(O.fp8_tiles(576)):
+            t = rows[r, lo:hi].astype(np.float64)
+            amax = np.max(np.abs(t))
+            if amax == 0:
+                assert scales[r, k] == 1.0 and np.all(codes[r, lo:hi] == 0)
+                continue
+            sc = float(scales[r, k])
+            assert np.frexp(sc)[0] == 0.5, "the scale is a power of two"
+            assert sc == 2.0 ** _smallest_pow2_exponent(amax)
+            assert 224.0 < amax / sc <= 448.0
+            assert np.array_equal(codes[r, lo:hi], _nearest_even_e4m3(t / sc))
+    assert scales[2, 0] == 2.0 ** -3
+    # the dequantised rows are the codes times their tile's power of two
+    deq = O.dequantize_fp8_rows(codes, scales)
+    err = np.abs(deq - rows)
+    assert np.all(err <= np.maximum(np.abs(rows) * 2.0 ** -4,
+                                    2.0 ** -10 * np.repeat(scales, [128] * 4 + [64], axis=1)) * 1.0001)
+
+
+def test_query_rows_e4m3_pow2():
+    """One power-of-two scale per row: rows of very different magnitude each
+    keep e4m3's relative precision."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((3, 2, 40)).astype(np.float32)
+    x[0, 1] *= 1e4
+    x[1, 0] *= 1e-5
+    x[2, 1] = 0.0
+    out = O.quantize_rows_e4m3_pow2(x)
+    assert out.shape == x.shape
+    for i in range(3):
+        for j in range(2):
+            row = x[i, j].astype(np.float64)
+            a = np.max(np.abs(row))
+            if a == 0:
+                assert np.all(out[i, j] == 0)
+                continue
+            e = _smallest_pow2_exponent(a)
+            want = O.e4m3_decode(_nearest_even_e4m3(row * 2.0 ** -e)) * 2.0 ** e
+            assert np.array_equal(out[i, j], want)
+            assert 224.0 < np.max(np.abs(out[i, j])) / 2.0 ** e <= 448.0
+
+
 # --------------------------------------------------------------------------
 # attention: brute force, un-absorbed form, library attention, special cases
 # --------------------------------------------------------------------------
