@@ -62,7 +62,12 @@ typedef enum mla_status {
 typedef enum mla_dtype {
   MLA_FP32 = 0,
   MLA_BF16 = 1,
-  MLA_FP8_E4M3 = 2 /* OCP E4M3 (max 448, no infinities); cache only */
+  MLA_FP8_E4M3 = 2, /* OCP E4M3 (max 448, no infinities); cache only */
+  /* The MLA_FP8_E4M3 layout (codes and one fp32 scale per (token, tile))
+   * with every scale a power of two: the append picks the smallest 2^E with
+   * max|tile| <= 448 * 2^E, and the matrix-core decode applies the scales
+   * inside its fp8 score products.  Cache only. */
+  MLA_FP8_E4M3_PO2 = 3
 } mla_dtype;
 
 /* Model dimensions, shared by every call.

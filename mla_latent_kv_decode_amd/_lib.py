@@ -15,7 +15,7 @@ from typing import Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla.so")
 
-FP32, BF16, FP8_E4M3 = 0, 1, 2
+FP32, BF16, FP8_E4M3, FP8_E4M3_PO2 = 0, 1, 2, 3
 FLAG_GENERIC_DECODE = 1
 FLAG_VALIDATE = 2
 

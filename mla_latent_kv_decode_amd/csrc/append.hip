@@ -100,6 +100,16 @@ __global__ __launch_bounds__(kApNT) void append_kernel(AppendArgs a) {
       for (int c = sub; c < ncols; c += 16) dst[c] = uint8_t(f32_to_e4m3(__fmul_rn(ys[tt][c], inv)));
       if (sub == 0) a.scales[row * ((D + 127) / 128) + blockIdx.y] = scale;
     }
+  } else if constexpr (CDT == MLA_FP8_E4M3_PO2) {
+    float amax = 0.f;
+    for (int c = sub; c < ncols; c += 16) amax = fmaxf(amax, fabsf(ys[tt][c]));
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const int e = amax > 0.f ? pow2_scale_exp(amax) : 0;
+    if (tok < a.n_tokens) {
+      uint8_t* dst = static_cast<uint8_t*>(a.cache) + row * D + n0;
+      for (int c = sub; c < ncols; c += 16) dst[c] = uint8_t(f32_to_e4m3(__builtin_ldexpf(ys[tt][c], -e)));
+      if (sub == 0) a.scales[row * ((D + 127) / 128) + blockIdx.y] = __builtin_ldexpf(1.0f, e);
+    }
   } else if constexpr (CDT == MLA_BF16) {
     if (tok < a.n_tokens) {
       uint16_t* dst = static_cast<uint16_t*>(a.cache) + row * D + n0;
@@ -129,10 +139,12 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   if (a.act_dtype == MLA_FP32) {
     if (a.cache_dtype == MLA_FP32) return launch_t<MLA_FP32, MLA_FP32>(a, st);
     if (a.cache_dtype == MLA_BF16) return launch_t<MLA_FP32, MLA_BF16>(a, st);
+    if (a.cache_dtype == MLA_FP8_E4M3_PO2) return launch_t<MLA_FP32, MLA_FP8_E4M3_PO2>(a, st);
     return launch_t<MLA_FP32, MLA_FP8_E4M3>(a, st);
   }
   if (a.cache_dtype == MLA_FP32) return launch_t<MLA_BF16, MLA_FP32>(a, st);
   if (a.cache_dtype == MLA_BF16) return launch_t<MLA_BF16, MLA_BF16>(a, st);
+  if (a.cache_dtype == MLA_FP8_E4M3_PO2) return launch_t<MLA_BF16, MLA_FP8_E4M3_PO2>(a, st);
   return launch_t<MLA_BF16, MLA_FP8_E4M3>(a, st);
 }
 

@@ -3,7 +3,8 @@
 // [c ; k^R] = h . [W^DKV ; W^KR]^T, rotate k^R (rotate-half pairs
 // (j, j + d_R/2), angle pos * base^(-j/(d_R/2)) in fp64, cos/sin rounded to
 // fp32; the host keeps the RoPE part inside one tile), then store the row in
-// the cache format (e4m3: the tile's amax sets the scale).
+// the cache format (e4m3: the tile's amax sets the scale, amax / 448 or the
+// smallest power of two that maps amax into (224, 448]).
 //
 // A 256-thread workgroup finalises two units, one per 128-thread half, so
 // the body can share a launch with other 256-thread work.
@@ -92,9 +93,15 @@ MLA_DEV void append_finalize_pair(const AppendArgs& a, const float* ws, int nk, 
     if (tid % kWave == 0) wmax[tid / kWave] = am;
     __syncthreads();
     const float amax = fmaxf(wmax[0], wmax[1]);
-    const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
-    if (st) static_cast<uint8_t*>(a.cache)[row * D + c] = uint8_t(f32_to_e4m3(__fmul_rn(v, inv)));
-    if (live && tid == 0) a.scales[row * ((D + 127) / 128) + tile] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if constexpr (CDT == MLA_FP8_E4M3_PO2) {  // scale 2^E, codes of v * 2^-E (exact scaling)
+      const int e = amax > 0.f ? pow2_scale_exp(amax) : 0;
+      if (st) static_cast<uint8_t*>(a.cache)[row * D + c] = uint8_t(f32_to_e4m3(__builtin_ldexpf(v, -e)));
+      if (live && tid == 0) a.scales[row * ((D + 127) / 128) + tile] = __builtin_ldexpf(1.0f, e);
+    } else {
+      const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+      if (st) static_cast<uint8_t*>(a.cache)[row * D + c] = uint8_t(f32_to_e4m3(__fmul_rn(v, inv)));
+      if (live && tid == 0) a.scales[row * ((D + 127) / 128) + tile] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    }
   }
 }
 

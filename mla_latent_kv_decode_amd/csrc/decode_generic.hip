@@ -134,7 +134,7 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
   if (a.act_dtype == MLA_FP32) {
     if (a.cache_dtype == MLA_FP32) return launch_generic<MLA_FP32, MLA_FP32>(a, st);
     if (a.cache_dtype == MLA_BF16) return launch_generic<MLA_BF16, MLA_FP32>(a, st);
-    return launch_generic<MLA_FP8_E4M3, MLA_FP32>(a, st);
+    return launch_generic<MLA_FP8_E4M3, MLA_FP32>(a, st);  // either e4m3 format: code * fp32 scale
   }
   if (a.cache_dtype == MLA_FP32) return launch_generic<MLA_FP32, MLA_BF16>(a, st);
   if (a.cache_dtype == MLA_BF16) return launch_generic<MLA_BF16, MLA_BF16>(a, st);

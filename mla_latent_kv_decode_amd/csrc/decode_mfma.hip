@@ -53,10 +53,22 @@
 //  * Before the plan, the workgroup already streams the Q of the sequence its
 //    first piece would belong to with equal lengths; the plan reads the
 //    lengths from an LDS window loaded ahead of that Q.
-//  * fp8 cache (kF8): each step's e4m3 codes and per-(token, 128-channel)
-//    scales land in a staging buffer and the workgroup dequantises them (code
-//    x scale in fp32, one bf16 rounding) into a bf16 step buffer one
-//    iteration ahead of use; from there the step is read as above.
+//  * e4m3 cache with tile scales of any value (mode 1): each step's codes
+//    and per-(token, 128-channel) scales land in a staging buffer and the
+//    workgroup dequantises them (code x scale in fp32, one bf16 rounding)
+//    into a bf16 step buffer one iteration ahead of use; from there the step
+//    is read as above.
+//  * e4m3 cache with power-of-two tile scales (mode 2): the scores run on
+//    v_mfma_scale_f32_32x32x64_f8f6f4 straight from the staged codes.  The
+//    MFMA applies each token's tile scale (its exponent byte, per A row) and
+//    Q is e4m3 under one power-of-two scale per head, folded into the
+//    softmax's log2 factor; both operands are exact, so only Q's rounding to
+//    e4m3 differs from the bf16 path.  V = code x 2^E is exact in bf16: the
+//    workgroup converts each step's latent codes with the scaled conversion
+//    instruction (two values per instruction) into a bf16 V buffer during
+//    the step's own output MFMAs, and the next step's barrier publishes it;
+//    the output product is the bf16 one above.  Half the score-side MFMA
+//    cycles and LDS bytes of the bf16 path, and no conversion pass of its own.
 #include <utility>
 
 #include "mla_internal.h"
@@ -88,14 +100,24 @@ constexpr int kStageRow = kDC * 2 + 16;       // epilogue transpose row (padded 
 constexpr int kQK = kD / 16;                  // score MFMAs per step
 constexpr int kPV = 2 * (kDC / 32);           // output MFMAs per step
 constexpr int kRK = 4, kRV = 4;               // LDS operand fragments read ahead of their MFMA
+// e4m3 with power-of-two scales: two bf16 V buffers (8 column groups of 1 KB
+// per 8-token group: the latent part only) and three code staging buffers
+// (steps h, h+1, h+2): codes as 9 regions of 2 KB, region n the 32 x 64-byte
+// A tile of score MFMA n, then the 1 KB scale load.
+constexpr int kVBytes = kStep * kDC * 2;                 // 32768
+constexpr int kF8Q = kD / 64;                            // fp8 score MFMAs per step (K = 64)
+constexpr int kP2Loads = kF8Loads + 1;                   // 18 code loads + 1 scale load per step
+constexpr int kP2LdsEnd = 2 * kVBytes + 3 * kF8Stage;    // 123904
 static_assert(4 * 32 * kStageRow <= kLdsBytes, "epilogue stage must fit the step buffers");
 static_assert(kF8NBuf * kStepBytes + 2 * kF8Stage <= kLdsBytes && kF8ScaleBytes <= 1024, "fp8 staging layout");
 static_assert(kNT / kWave == kNBuf && kH * kRowBytes <= kLdsBytes, "Q is staged through the step buffers");
+static_assert(kP2LdsEnd <= kLdsBytes && kP2Loads <= 5 * (kNT / kWave), "power-of-two fp8 layout");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // 16-byte-chunk swizzle: chunk slot (c & 7) ^ swz(t) within token t's sub-row.
@@ -105,6 +127,16 @@ MLA_DEV int swz(int t) { return ((((t & 3) << 1) | ((t >> 2) & 1)) ^ ((t >> 2) &
 MLA_DEV int step_off(int t, int c) {
   return (((t >> 3) * 9 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz(t))) * 16;
 }
+
+// Byte offset of bf16 chunk c (0..63) of token t in a latent-only V buffer
+// (the step layout with 8 column groups instead of 9).
+MLA_DEV int v8_off(int t, int c) {
+  return (((t >> 3) * 8 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz(t))) * 16;
+}
+// Code staging of a power-of-two fp8 step: 16-byte chunk c (0..3) of token t
+// in region n sits in slot c ^ cswz(t) of the token's 64-byte row, so that 16
+// consecutive tokens read at one chunk index cover all banks.
+MLA_DEV int cswz(int t) { return (t >> 2) & 3; }
 
 constexpr int kPtab = 1024;  // page-table entries of a piece staged in LDS at a time
 
@@ -214,6 +246,31 @@ MLA_DEV void load_step_f8(unsigned char* dst, const unsigned char* codes, const 
   }
 }
 
+// Load m (0..4) of this wave's share of a power-of-two fp8 step: code load
+// k = wave + 4m (region k / 2, token half k % 2 = wave % 2) or, for k = 18,
+// the 640 bytes of scales; wave 3 has four loads.  Lane i of a code load
+// fills slot i % 4 of token 16 * (k % 2) + i / 4 (voff: that token's source
+// chunk, wave-fixed); the region's column offset goes into soffset.
+MLA_DEV void load_piece_p2(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, unsigned char* dst,
+                           int wave, int voff, int lane, int m) {
+  const int k = wave + 4 * m;
+  if (m < 4 || wave < 2) {  // k < 18: a code load
+    const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(dst + k * 1024)));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rc), "s"((k >> 1) * 64), "{m0}"(lds)
+                 : "memory");
+  } else if (wave == 2) {  // k == 18: the scales
+    const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(dst + kF8Codes)));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(lane * 16), "s"(rs), "{m0}"(lds)
+                 : "memory");
+  }
+}
+
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 MLA_DEV uint32_t lds_addr(const unsigned char* p) {
@@ -274,6 +331,32 @@ MLA_DEV void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 MLA_DEV void scores_ready(f32x16& s) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s)); }
+// fp8 score MFMA with the A rows' scales taken from byte J of `sa` (E8M0:
+// 2^(byte - 127)) and unit B scales (byte 127 of `sb`).  The scale registers
+// are written by VALU code ahead of the chain; scales_ready() puts three wait
+// states between those writes and the first MFMA that reads them.
+template <int J>
+MLA_DEV void mfma_qk8(f32x16& acc, const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb) {
+  if constexpr (J == 0)
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+        : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  else if constexpr (J == 1)
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,0,0] op_sel_hi:[0,0,0]"
+        : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  else if constexpr (J == 2)
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,0,0]"
+        : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  else
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+MLA_DEV void mfma_qk8_first(f32x16& acc, const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb) {
+  asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+      : "=&v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+MLA_DEV void scales_ready(uint32_t& a, uint32_t& b, uint32_t& c) {
+  asm volatile("s_nop 2" : "+v"(a), "+v"(b), "+v"(c));
+}
 // Output MFMAs with the accumulator pinned to AGPRs: left to itself the
 // register allocator keeps some O blocks in VGPRs and copies them into AGPRs
 // around every MFMA, which pushes Q out of registers.  Consecutive updates of
@@ -298,16 +381,22 @@ MLA_DEV void o_ready(f32x16 (&O)[16]) {
                  "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
 }
 
-template <bool kF8>
+// kMode: 0 bf16 cache, 1 e4m3 cache with any tile scales, 2 e4m3 cache with
+// power-of-two tile scales.
+template <int kMode>
 __global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a) {
+  constexpr bool kF8 = kMode == 1, kP2 = kMode == 2;
   extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   constexpr int NB = kF8 ? kF8NBuf : kNBuf;  // bf16 step buffers in the ring
+  constexpr int kTG = kP2 ? 8 * 1024 : 9 * 1024;  // V: bytes per 8-token group
   auto bbuf = [&](int i) __attribute__((always_inline)) { return sm.lds + i * kStepBytes; };
   auto stage_buf = [&](int i) __attribute__((always_inline)) {
     return sm.lds + kF8NBuf * kStepBytes + i * kF8Stage;
   };
+  auto vbuf = [&](int i) __attribute__((always_inline)) { return sm.lds + i * kVBytes; };      // mode 2
+  auto cbuf = [&](int i) __attribute__((always_inline)) { return sm.lds + 2 * kVBytes + i * kF8Stage; };
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -339,6 +428,17 @@ void decode_mfma_kernel(DecodeArgs a) {
   // bf16: kept in two registers for the whole kernel.  fp8: recomputed from
   // a fresh lane id at every step -- two registers fewer across the loop,
   // which the dequantisation needs to stay spill-free.
+  auto voff0_of8 = [](int l) __attribute__((always_inline)) {
+    const int gg = l >> 5, hh = (l >> 4) & 1, ss = l & 15;
+    return uint32_t(v8_off(4 * gg + (ss >> 2), 2 * hh + ((ss & 3) >> 1)) + 8 * (ss & 1));
+  };
+  // mode 2: the score A fragment of lane (g, hl) is chunks 2g, 2g+1 of token
+  // hl's 64-byte row of a region (the second at XOR 16).  Recomputed from a
+  // fresh lane id where used, like the V offsets: no register across the loop.
+  auto koff8_of = [](int l) __attribute__((always_inline)) {
+    const int t = l & 31;
+    return uint32_t(t * 64 + (((2 * (l >> 5)) ^ cswz(t)) << 4));
+  };
   const uint32_t koff0 = koff0_of(lane), voff0 = voff0_of(lane);
   auto koff0_at = [&]() __attribute__((always_inline)) {
     if constexpr (kF8) return koff0_of(tid_fresh() & (kWave - 1)); else return koff0;
@@ -347,6 +447,11 @@ void decode_mfma_kernel(DecodeArgs a) {
     if constexpr (kF8) return voff0_of(tid_fresh() & (kWave - 1)); else return voff0;
   };
   const int loff = load_lane_off(lane, wave & 1);
+  // mode 2: this lane's source chunk in its code loads (token 16 (wave % 2) + lane / 4)
+  auto loff8_at = [&]() __attribute__((always_inline)) {
+    const int l = tid_fresh() % kWave, t = 16 * (wave & 1) + l / 4;
+    return t * kD + (((l & 3) ^ cswz(t)) << 4);
+  };
 
   // Speculative Q: with equal lengths, partition `part`'s first piece belongs
   // to sequence part * B / G, so that sequence's Q starts streaming into the
@@ -421,19 +526,72 @@ void decode_mfma_kernel(DecodeArgs a) {
     wait_vm<0>();
     step_barrier();
     const int blk0 = block_of(0);  // steps 0 and 1 lie in the piece's first block
-    bf16x8 qf[kQK];
-    {
+    bf16x8 qf[kP2 ? 1 : kQK];
+    i32x8 qf8[kP2 ? kF8Q : 1];
+    float c_l2 = c_log2;  // scores -> log2 units (mode 2: times the head's Q scale)
+    if constexpr (!kP2) {
       // (addresses from a fresh lane id: not kept live across the step loop)
       const int ql = tid_fresh() % kWave;
       const uint32_t qb = lds_addr(bbuf(wave)) + uint32_t(step_off(ql % 32, ql / 32));
 #pragma unroll
       for (int s = 0; s < kQK; ++s) qf[s] = lds_b128_at((qb ^ uint32_t((s & 3) << 5)) + uint32_t((s >> 2) * 1024));
+    } else {
+      // Q of head hl in e4m3 under one power-of-two scale 2^E (the smallest
+      // with max |q| <= 448 * 2^E): lane (g, hl) holds channels 64 n + 32 g
+      // .. + 31 of score MFMA n, which are bf16 chunks 8 n + 4 g + k (k < 4)
+      // of the staged row.  Pass 1 takes the head's max |q| (the other half
+      // of the row is in lane ^ 32), pass 2 scales and converts.
+      const int ql = tid_fresh() % kWave, qg = ql / 32, qh = ql % 32;
+      const uint32_t qb = lds_addr(bbuf(wave)) + uint32_t(step_off(qh, 4 * qg));  // chunk 4 qg (+ k: XOR k << 4)
+      float amax = 0.f;
+      for (int n = 0; n < kF8Q; ++n)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bf16x8 v = lds_b128_at((qb ^ uint32_t(k << 4)) + uint32_t(n * 1024));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(float(v[e])));
+        }
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+      amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const int qe = amax > 0.f ? pow2_scale_exp(amax) : 0;
+      const float down = __builtin_ldexpf(1.0f, -qe);
+      c_l2 = __builtin_ldexpf(c_log2, qe);
+#pragma unroll
+      for (int n = 0; n < kF8Q; ++n)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bf16x8 v = lds_b128_at((qb ^ uint32_t(k << 4)) + uint32_t(n * 1024));
+          int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(float(v[0]) * down, float(v[1]) * down, 0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(float(v[2]) * down, float(v[3]) * down, w0, true);
+          int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(float(v[4]) * down, float(v[5]) * down, 0, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(float(v[6]) * down, float(v[7]) * down, w1, true);
+          qf8[n][2 * k] = w0;
+          qf8[n][2 * k + 1] = w1;
+        }
     }
     step_barrier();  // every wave holds its Q: the buffers are free for the cache
-    if constexpr (kF8)
+    // mode 2: descriptors of step s's codes and scales (empty past the piece:
+    // the loads then write zeros into a free buffer)
+    auto rsrc_codes = [&](int blk, int s_, bool live) __attribute__((always_inline)) {
+      return __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(cache + int64_t(blk) * (kBS * kD) + (s_ & 1) * kF8Codes), (short)0, live ? valid_in(s_) * kD : 0,
+          0x00020000);
+    };
+    auto rsrc_scales = [&](int blk, int s_, bool live) __attribute__((always_inline)) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + (int64_t(blk) * kBS + (s_ & 1) * kStep) * 5),
+                                               (short)0, live ? kF8ScaleBytes : 0, 0x00020000);
+    };
+    if constexpr (kF8) {
       load_f8(0, blk0, 0, valid_in(0));
-    else
+    } else if constexpr (kP2) {
+      for (int s_ = 0; s_ < 2; ++s_) {
+        const auto rc = rsrc_codes(blk0, s_, s_ < nsteps), rs = rsrc_scales(blk0, s_, s_ < nsteps);
+#pragma unroll
+        for (int m = 0; m < 5; ++m) load_piece_p2(rc, rs, cbuf(s_), wave, loff8_at(), lane, m);
+      }
+    } else {
       load_step(bbuf(0), step_at(blk0, 0), valid_in(0), wave, loff);
+    }
 
     f32x16 O[kDC / 32];
     {
@@ -449,10 +607,13 @@ void decode_mfma_kernel(DecodeArgs a) {
     // V^T . P^T for step h-1 (32 MFMAs), with the softmax of step h spread
     // between them, so the exp/max VALU work runs under matrix work.  The
     // first step has no PV yet; the drain after the last step has no QK.
-    auto run_step = [&](auto qk_on, auto pv_on, int h, auto&& after_qk_mfma) __attribute__((always_inline)) {
+    auto run_step = [&](auto qk_on, auto pv_on, int h, auto&& after_qk_mfma, auto&& after_pv_mfma)
+                        __attribute__((always_inline)) {
       constexpr bool kQKOn = decltype(qk_on)::value, kPVOn = decltype(pv_on)::value;
-      const uint32_t kb = lds_addr(bbuf(h % NB)) + koff0_at();
-      const uint32_t vb = lds_addr(bbuf(h > 0 ? (h + NB - 1) % NB : 0)) + voff0_at();
+      const uint32_t kb = kP2 ? lds_addr(cbuf(h % 3)) + koff8_of(tid_fresh() % kWave)
+                              : lds_addr(bbuf(h % NB)) + koff0_at();
+      const uint32_t vb = kP2 ? lds_addr(vbuf((h + 1) & 1)) + voff0_of8(tid_fresh() % kWave)
+                              : lds_addr(bbuf(h > 0 ? (h + NB - 1) % NB : 0)) + voff0_at();
       auto kfrag = [&](int n) __attribute__((always_inline)) {  // chunk pair n&3 of sub-block column n>>2
         return lds_b128_at((kb ^ uint32_t((n & 3) << 5)) + uint32_t((n >> 2) * 1024));
       };
@@ -462,13 +623,70 @@ void decode_mfma_kernel(DecodeArgs a) {
       // file traffic, which shows up as a higher sustained clock)
       auto vfrag = [&](int n) __attribute__((always_inline)) {
         const int i = n & 1, cb = n >> 1;
-        const uint32_t base = uint32_t((2 * i) * 9216 + (cb >> 1) * 1024);  // token rows 16i..16i+15
+        const uint32_t base = uint32_t((2 * i) * kTG + (cb >> 1) * 1024);  // token rows 16i..16i+15
         const uint32_t v = vb ^ uint32_t((cb & 1) << 6);
-        return lds_tr_pair_at(v + base, (v ^ 32u) + base + 9216u);
+        return lds_tr_pair_at(v + base, (v ^ 32u) + base + uint32_t(kTG));
       };
       f32x16 S;
       bf16x8 vr[kRV];
-      if constexpr (kQKOn) {
+      // mode 2: this lane's token hl of step h -- its five tile scales give the
+      // score MFMAs' A scales (exponent bytes; 127 = 1 past the length) and the
+      // V conversion's scales (tiles 0..3 of the same token)
+      const int nv = kQKOn ? valid_in(h) : kStep;
+      float vsc[4];
+      if constexpr (kP2 && kQKOn) {
+        typedef __attribute__((address_space(3))) const float lds_f32;
+        const int sl = tid_fresh() % 32;
+        const uint32_t sbase = lds_addr(cbuf(h % 3)) + uint32_t(kF8Codes + sl * 20);
+        const bool live = sl < nv;
+        uint32_t sa0 = 0, sa1, sb = 127u;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+          const float sc = *(lds_f32*)(uintptr_t)(sbase + 4 * j);
+          const uint32_t e = live ? (__float_as_uint(sc) >> 23) & 0xffu : 127u;
+          if (j < 4) {
+            sa0 |= e << (8 * j);
+            vsc[j] = live ? sc : 1.0f;
+          } else {
+            sa1 = e;
+          }
+        }
+        scales_ready(sa0, sa1, sb);
+        auto kfrag8 = [&](int n) __attribute__((always_inline)) {  // A tile of score MFMA n
+          const bf16x8 lo = lds_b128_at(kb + uint32_t(n * 2048));
+          const bf16x8 hi = lds_b128_at((kb ^ 16u) + uint32_t(n * 2048));
+          const u32x4 l4 = __builtin_bit_cast(u32x4, lo), h4 = __builtin_bit_cast(u32x4, hi);
+          return i32x8{int(l4[0]), int(l4[1]), int(l4[2]), int(l4[3]), int(h4[0]), int(h4[1]), int(h4[2]), int(h4[3])};
+        };
+        constexpr int kR8 = 3;
+        i32x8 kr[kR8];
+#pragma unroll
+        for (int n = 0; n < kR8; ++n) {
+          kr[n] = kfrag8(n);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int n = 0; n < kF8Q; ++n) {
+          if (n == 0) mfma_qk8_first(S, kr[0], qf8[0], sa0, sb);
+          else if (n == 8) mfma_qk8<0>(S, kr[n % kR8], qf8[n], sa1, sb);
+          else if (n >> 1 == 0) mfma_qk8<0>(S, kr[n % kR8], qf8[n], sa0, sb);
+          else if (n >> 1 == 1) mfma_qk8<1>(S, kr[n % kR8], qf8[n], sa0, sb);
+          else if (n >> 1 == 2) mfma_qk8<2>(S, kr[n % kR8], qf8[n], sa0, sb);
+          else mfma_qk8<3>(S, kr[n % kR8], qf8[n], sa0, sb);
+          if (n + kR8 < kF8Q) {
+            kr[n % kR8] = kfrag8(n + kR8);
+          } else if constexpr (kPVOn) {
+            const int v = n + kR8 - kF8Q;
+            if (v < kRV) vr[v] = vfrag(v);
+          }
+          after_qk_mfma(n);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (kPVOn) {
+#pragma unroll
+          for (int v = kR8; v < kRV; ++v) vr[v] = vfrag(v);
+        }
+      } else if constexpr (kQKOn) {
         bf16x8 kr[kRK];
 #pragma unroll
         for (int n = 0; n < kRK; ++n) {  // in order: the first MFMA waits only for the first read
@@ -495,6 +713,34 @@ void decode_mfma_kernel(DecodeArgs a) {
         for (int n = 0; n < kRV; ++n) vr[n] = vfrag(n);
       }
 
+      // mode 2: step h's latent codes -> bf16 V buffer h % 2, four 16-code
+      // chunks per lane (token hl, chunk 2 wave + g + 8 i of tile i),
+      // interleaved with the output MFMAs below
+      u32x4 cq;
+      auto v_read = [&](int i) __attribute__((always_inline)) {
+        typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+        const int dl = tid_fresh() % kWave, dg = (2 * wave + dl / 32), dt = dl % 32;
+        const uint32_t addr = lds_addr(cbuf(h % 3)) + uint32_t((dg >> 2) * 2048 + i * 4096 + dt * 64 +
+                                                                (((dg & 3) ^ cswz(dt)) << 4));
+        cq = *(lds_u4*)(uintptr_t)addr;
+      };
+      auto v_write = [&](int i) __attribute__((always_inline)) {
+        typedef __attribute__((address_space(3))) u32x4 lds_u4w;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const int dl = tid_fresh() % kWave, dg = (2 * wave + dl / 32), dt = dl % 32;
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(cq[e]), vsc[i], false);
+          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(cq[e]), vsc[i], true);
+          o[2 * e] = __builtin_bit_cast(uint32_t, lo);
+          o[2 * e + 1] = __builtin_bit_cast(uint32_t, hi);
+        }
+        const uint32_t addr = lds_addr(vbuf(h & 1)) + uint32_t(v8_off(dt, 2 * dg) + i * 2048);
+        *(lds_u4w*)(uintptr_t)addr = u32x4{o[0], o[1], o[2], o[3]};
+        *(lds_u4w*)(uintptr_t)(addr ^ 16u) = u32x4{o[4], o[5], o[6], o[7]};
+      };
+
       // softmax of step h in pieces (lane = one head; tokens 8*(r/4) + 4*g + r%4):
       // p = 2^(s' - m_ref) against the head's current reference, without
       // first taking the step's maximum.  Whether a p left the headroom is
@@ -502,7 +748,6 @@ void decode_mfma_kernel(DecodeArgs a) {
       // NaN); that -- and the piece's first step, whose reference is still
       // -inf -- takes the exact path below, which recomputes the step against
       // its maximum.
-      const int nv = kQKOn ? valid_in(h) : kStep;
       float lsum = 0.f, lsum2 = 0.f;
       auto softmax_part = [&](int k) __attribute__((always_inline)) {
         if constexpr (kQKOn) {
@@ -514,8 +759,8 @@ void decode_mfma_kernel(DecodeArgs a) {
           }
           if (k >= 2 && k < 10) {
             const int i = (k - 2) >> 2, e = 2 * ((k - 2) & 3);
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_log2, -m_ref));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e + 1], c_log2, -m_ref));
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_l2, -m_ref));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e + 1], c_l2, -m_ref));
             lsum += p0;   // two running sums: half the dependent chain
             lsum2 += p1;
             p_cur[i][e / 2] = pack_bf16x2(p0, p1);
@@ -532,11 +777,23 @@ void decode_mfma_kernel(DecodeArgs a) {
           mfma_pv(O[n >> 1], vr[n % kRV], p_prev[n & 1]);
           if (n + kRV < kPV) vr[n % kRV] = vfrag(n + kRV);
           softmax_part(n);
+          if constexpr (kP2 && kQKOn) {
+            if (n >= 10 && n < 26 && (n - 10) % 4 == 0) v_read((n - 10) / 4);
+            if (n >= 12 && n < 28 && (n - 12) % 4 == 0) v_write((n - 12) / 4);
+          }
+          after_pv_mfma(n);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
         for (int k = 0; k < 10; ++k) softmax_part(k);
+        if constexpr (kP2 && kQKOn) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v_read(i);
+            v_write(i);
+          }
+        }
       }
       if constexpr (kQKOn) {
         if (h == 0 || __any(!(lsum + lsum2 <= kPSumLimit))) {
@@ -550,7 +807,7 @@ void decode_mfma_kernel(DecodeArgs a) {
           const float a4 = fmaxf(fmaxf(S[12], S[13]), S[14]);
           float mx = fmaxf(fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)), fmaxf(a4, S[15]));
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c_log2;
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c_l2;
           const float m_new = h == 0 ? mx : fmaxf(m_ref, mx);
           const float corr = h == 0 ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
           m_ref = m_new;
@@ -559,8 +816,8 @@ void decode_mfma_kernel(DecodeArgs a) {
           for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_log2, -m_ref));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e + 1], c_log2, -m_ref));
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e], c_l2, -m_ref));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * i + e + 1], c_l2, -m_ref));
               lsum += p0;
               lsum2 += p1;
               p_cur[i][e / 2] = pack_bf16x2(p0, p1);
@@ -601,7 +858,7 @@ void decode_mfma_kernel(DecodeArgs a) {
       blk_nx = block_of((h + 3) >> 1);
     };
     auto no_hook = [](int) __attribute__((always_inline)) {};
-    if constexpr (!kF8) {
+    if constexpr (kMode == 0) {
       if (nsteps > 1) load_step(bbuf(1), step_at(blk0, 1), valid_in(1), wave, loff);
       // Iteration h: wait until step h's own loads are done (at most the loads
       // of step h+1, issued one iteration earlier, still pending); a barrier
@@ -633,8 +890,32 @@ void decode_mfma_kernel(DecodeArgs a) {
         run_step(std::true_type{}, std::true_type{}, h, [&](int n) __attribute__((always_inline)) {
           if (n % 4 == 1) load_piece(r, dst, wave, loff, n / 4);
           if (n == 2 && nx) blk_raw = sm.ptab[((h + 3) >> 1) - pbase];
+        }, no_hook);
+      }
+    } else if constexpr (kP2) {
+      // Iteration h: step h's codes have landed (at most the next step's
+      // loads, 4 or 5 per wave, still pending) and the barrier also publishes
+      // V of step h-1 and frees code buffer (h+2) % 3 and V buffer h % 2.
+      // Scores of step h, then the output MFMAs of step h-1 with the softmax
+      // of step h, the conversion of step h's V and the loads of step h+2
+      // spread between them.
+      int blk_raw = 0;
+      for (int h = 0; h < nsteps; ++h) {
+        wait_vm<4>();
+        step_barrier();
+        if (h > 0) blk_nx = __builtin_amdgcn_readfirstlane(blk_raw);
+        const bool nx = h + 3 < nsteps;
+        if (nx) ptab_window((h + 3) >> 1);
+        const bool ld = h + 2 < nsteps;
+        const auto rc = rsrc_codes(ld ? blk_nx : 0, h + 2, ld), rs = rsrc_scales(ld ? blk_nx : 0, h + 2, ld);
+        unsigned char* const dst = cbuf((h + 2) % 3);
+        run_step(std::true_type{}, std::true_type{}, h, [&](int n) __attribute__((always_inline)) {
+          if (n == 2 && nx) blk_raw = sm.ptab[((h + 3) >> 1) - pbase];
+        }, [&](int n) __attribute__((always_inline)) {
+          if (n % 6 == 2) load_piece_p2(rc, rs, dst, wave, loff8_at(), tid_fresh() % kWave, n / 6);
         });
       }
+      step_barrier();  // V of the last step is complete
     } else {
       // fp8: step h's codes land in staging buffer h%2 and are dequantised
       // into bf16 step buffer h%3 at the end of iteration h-1, which then
@@ -652,7 +933,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         step_barrier();  // step h converted; staging buffer h%2 free again
         if (h + 2 < nsteps) load_f8(h & 1, blk_nx, h + 2, valid_in(h + 2));
         if (h + 3 < nsteps) next_block(h);
-        run_step(std::true_type{}, std::true_type{}, h, no_hook);
+        run_step(std::true_type{}, std::true_type{}, h, no_hook, no_hook);
         if (h + 1 < nsteps) {
           if (h + 2 < nsteps)
             wait_vm<4>();
@@ -663,7 +944,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     }
-    run_step(std::false_type{}, std::true_type{}, nsteps, no_hook);  // PV of the last step
+    run_step(std::false_type{}, std::true_type{}, nsteps, no_hook, no_hook);  // PV of the last step
     wait_vm<0>();  // the last iterations' empty loads, before the LDS is reused
     o_ready(O);
     __syncthreads();  // buffers are reused by the epilogue stage
@@ -705,24 +986,26 @@ void decode_mfma_kernel(DecodeArgs a) {
 bool decode_mfma_supported(const DecodeArgs& a) {
   const bool cache_ok =
       a.cache_dtype == MLA_BF16 ||
-      (a.cache_dtype == MLA_FP8_E4M3 && a.scales != nullptr && (reinterpret_cast<uintptr_t>(a.scales) % 16) == 0);
+      (is_fp8_cache(a.cache_dtype) && a.scales != nullptr && (reinterpret_cast<uintptr_t>(a.scales) % 16) == 0);
   return a.H == kH && a.d_latent == kDC && a.D == kD && a.block_size == kBS && a.act_dtype == MLA_BF16 &&
          cache_ok && (reinterpret_cast<uintptr_t>(a.cache) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.q) % 16) == 0;
 }
 
-template <bool kF8>
+template <int kMode>
 hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t st) {
   const size_t smem = sizeof(Smem);
-  if (hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(decode_mfma_kernel<kF8>), int(smem));
+  if (hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(decode_mfma_kernel<kMode>), int(smem));
       e != hipSuccess)
     return e;
   dim3 grid(unsigned(a.G) * unsigned(a.n_q));
-  hipLaunchKernelGGL(decode_mfma_kernel<kF8>, grid, dim3(kNT), smem, st, a);
+  hipLaunchKernelGGL(decode_mfma_kernel<kMode>, grid, dim3(kNT), smem, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
-  return a.cache_dtype == MLA_FP8_E4M3 ? launch_decode_mfma_t<true>(a, st) : launch_decode_mfma_t<false>(a, st);
+  if (a.cache_dtype == MLA_FP8_E4M3_PO2) return launch_decode_mfma_t<2>(a, st);
+  if (a.cache_dtype == MLA_FP8_E4M3) return launch_decode_mfma_t<1>(a, st);
+  return launch_decode_mfma_t<0>(a, st);
 }
 
 }  // namespace mla

@@ -278,6 +278,8 @@ hipError_t launch_append_mfma(const AppendArgs& a, void* ws, hipStream_t st) {
     hipLaunchKernelGGL(append_finalize_kernel<MLA_BF16>, g2, dim3(kNT), 0, st, a, w, nk);
   else if (a.cache_dtype == MLA_FP32)
     hipLaunchKernelGGL(append_finalize_kernel<MLA_FP32>, g2, dim3(kNT), 0, st, a, w, nk);
+  else if (a.cache_dtype == MLA_FP8_E4M3_PO2)
+    hipLaunchKernelGGL(append_finalize_kernel<MLA_FP8_E4M3_PO2>, g2, dim3(kNT), 0, st, a, w, nk);
   else
     hipLaunchKernelGGL(append_finalize_kernel<MLA_FP8_E4M3>, g2, dim3(kNT), 0, st, a, w, nk);
   return hipGetLastError();

@@ -50,7 +50,7 @@ int check_dims(const mla_dims* d, bool need_cache_dtype) {
   if (d->block_size < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "block_size=%d", d->block_size);
   if (d->act_dtype != MLA_FP32 && d->act_dtype != MLA_BF16)
     return fail(MLA_ERR_INVALID_ARGUMENT, "act_dtype=%d must be MLA_FP32 or MLA_BF16", d->act_dtype);
-  if (need_cache_dtype && (d->cache_dtype < MLA_FP32 || d->cache_dtype > MLA_FP8_E4M3))
+  if (need_cache_dtype && (d->cache_dtype < MLA_FP32 || d->cache_dtype > MLA_FP8_E4M3_PO2))
     return fail(MLA_ERR_INVALID_ARGUMENT, "cache_dtype=%d", d->cache_dtype);
   if (d->softmax_scale <= 0.f && d->d_nope + d->d_rope <= 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "default softmax scale needs d_nope + d_rope > 0");
@@ -238,7 +238,7 @@ int append_prepare(const mla_dims* d, const void* h, int32_t n_tokens, int32_t d
   if (n_tokens == 0) return MLA_OK;
   if (!h || !w_dkv || !seq_ids || !positions || !page_table || !cache || (d->d_rope > 0 && !w_kr))
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  if ((d->cache_dtype == MLA_FP8_E4M3) != (cache_scales != nullptr))
+  if (mla::is_fp8_cache(d->cache_dtype) != (cache_scales != nullptr))
     return fail(MLA_ERR_INVALID_ARGUMENT, "cache_scales must be given exactly for the fp8 cache");
   const size_t ae = elem_bytes(d->act_dtype), ce = elem_bytes(d->cache_dtype);
   if (!aligned(h, ae) || !aligned(w_dkv, ae) || (w_kr && !aligned(w_kr, ae)) || !aligned(cache, ce) ||
@@ -387,7 +387,7 @@ int mla_decode(const mla_dims* d, const void* q, int32_t batch, int32_t n_q, con
   if (batch == 0) return ok();
   if (!q || !cache || !page_table || !seq_lens || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  if ((d->cache_dtype == MLA_FP8_E4M3) != (cache_scales != nullptr))
+  if (mla::is_fp8_cache(d->cache_dtype) != (cache_scales != nullptr))
     return fail(MLA_ERR_INVALID_ARGUMENT, "cache_scales must be given exactly for the fp8 cache");
   const size_t ae = elem_bytes(d->act_dtype), ce = elem_bytes(d->cache_dtype);
   if (!aligned(q, ae) || !aligned(cache, ce) || !aligned(page_table, 4) || !aligned(seq_lens, 4) ||

@@ -49,6 +49,23 @@ MLA_DEV float e4m3_to_f32(uint32_t c) {
 }
 
 // fp32 -> E4M3, round to nearest even, magnitudes >= 448 saturate to 448.
+// Either e4m3 cache format (tile scales of any value, or powers of two).
+MLA_HD inline bool is_fp8_cache(int dt) { return dt == MLA_FP8_E4M3 || dt == MLA_FP8_E4M3_PO2; }
+
+// Exponent E of a power-of-two tile scale: the smallest integer with
+// amax <= 448 * 2^E (amax > 0 and finite).  With amax = 1.m * 2^e and
+// 448 = 1.75 * 2^8 that is e - 8, or e - 7 when 1.m > 1.75.
+MLA_DEV int pow2_scale_exp(float amax) {
+  int bias = 0;
+  if (amax < 1.17549435e-38f) {  // subnormal: normalise first (exact)
+    amax *= 18446744073709551616.0f;  // 2^64
+    bias = 64;
+  }
+  const uint32_t u = __float_as_uint(amax);
+  const int e = int((u >> 23) & 0xffu) - 127;
+  return (e - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0)) - bias;
+}
+
 MLA_DEV uint32_t f32_to_e4m3(float x) {
   uint32_t u = __float_as_uint(x);
   uint32_t sign = (u >> 24) & 0x80u;

@@ -305,6 +305,8 @@ hipError_t launch_append_finalize_query_mfma(const AppendArgs& ap, const void* w
     hipLaunchKernelGGL(append_finalize_query_kernel<MLA_BF16>, grid, dim3(kNT), 0, st, ap, w, nk, q, nq);
   else if (ap.cache_dtype == MLA_FP32)
     hipLaunchKernelGGL(append_finalize_query_kernel<MLA_FP32>, grid, dim3(kNT), 0, st, ap, w, nk, q, nq);
+  else if (ap.cache_dtype == MLA_FP8_E4M3_PO2)
+    hipLaunchKernelGGL(append_finalize_query_kernel<MLA_FP8_E4M3_PO2>, grid, dim3(kNT), 0, st, ap, w, nk, q, nq);
   else
     hipLaunchKernelGGL(append_finalize_query_kernel<MLA_FP8_E4M3>, grid, dim3(kNT), 0, st, ap, w, nk, q, nq);
   return hipGetLastError();

@@ -59,7 +59,7 @@ class Config:
     batch: int
     n_q: int
     seed: int
-    cache_dtype: str          # "fp32" | "bf16" | "fp8"
+    cache_dtype: str          # "fp32" | "bf16" | "fp8" | "fp8p2" (e4m3, power-of-two tile scales)
     act_dtype: str            # "fp32" | "bf16"
     seq_len: Optional[int]    # uniform length, or None for the ragged mix
     len_lo: int = 0
@@ -75,6 +75,9 @@ CONFIGS = {
     "ragged": Config("ragged", V3, 256, 2, 3, "bf16", "bf16", None, 512, 32768),
     "fp8": Config("fp8", V3, 128, 1, 4, "fp8", "bf16", 16384, outlier_frac=0.01,
                   outlier_gain=20.0),
+    # the fp8 workload's rows (same seed) with power-of-two tile scales
+    "fp8p2": Config("fp8p2", V3, 128, 1, 4, "fp8p2", "bf16", 16384, outlier_frac=0.01,
+                    outlier_gain=20.0),
 }
 
 

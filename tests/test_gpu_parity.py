@@ -14,7 +14,7 @@ import torch
 
 import mla_workloads as W
 from oracle import mla_oracle as O
-from tests.cases import (DT, DecodeCase, append_workspace, compare_sampled, dims_of, fp8_score_bound,
+from tests.cases import (DT, FP8, DecodeCase, append_workspace, compare_sampled, dims_of, fp8_score_bound,
                          max_abs, rel_l2, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -287,7 +287,7 @@ def test_query_absorb_mfma_agrees_with_generic():
 # --------------------------------------------------------------------------
 # append: placement is bit-exact (identity projection), values match the oracle
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("cache_dtype", ["fp32", "bf16", "fp8"])
+@pytest.mark.parametrize("cache_dtype", ["fp32", "bf16", "fp8", "fp8p2"])
 def test_append_identity_projection_bit_exact(cache_dtype):
     import mla_latent_kv_decode_amd as M
     d_c, d_r, bs = 512, 64, 64
@@ -313,7 +313,7 @@ def test_append_identity_projection_bit_exact(cache_dtype):
     w_kr = np.concatenate([np.zeros((d_r, d_c)), np.eye(d_r)], 1)
     cfg = W.Config("ident", W.Dims(1, d_c, d_r, 128, 128, D), 3, 1, 0, cache_dtype, act, None)
     dims = dims_of(cfg)
-    if cache_dtype == "fp8":
+    if cache_dtype in FP8:
         cache = torch.full((nblk, bs, D), 0x7F, dtype=torch.uint8, device="cuda")
         scales = torch.full((nblk, bs, 5), float("nan"), device="cuda")
     else:
@@ -330,8 +330,9 @@ def test_append_identity_projection_bit_exact(cache_dtype):
         blk, off = O.slot_of(table, int(seq_ids[i]), int(positions[i]), bs)
         written[blk, off] = True
         want = O.kv_rows(h64[i:i + 1], w_dkv, w_kr, positions[i:i + 1])[0].astype(np.float32)
-        if cache_dtype == "fp8":
-            codes, sc = O.quantize_fp8_row(want)
+        if cache_dtype in FP8:
+            codes, sc = O.quantize_fp8_rows(want[None], pow2_scales=cache_dtype == "fp8p2")
+            codes, sc = codes[0], sc[0]
             got_c = cache[blk, off].cpu().numpy()
             got_s = scales[blk, off].cpu().numpy()
             # latent tiles: exact inputs -> the same fp32 decisions -> identical bytes
@@ -354,7 +355,7 @@ def test_append_identity_projection_bit_exact(cache_dtype):
             assert np.all(np.abs(got[d_c:] - want[d_c:]) <= bound)
     untouched = torch.from_numpy(~written).cuda()
     a, b = cache[untouched], before[untouched]
-    if cache_dtype == "fp8":
+    if cache_dtype in FP8:
         assert torch.equal(a, b)
         assert torch.isnan(scales[untouched]).all()
     else:
@@ -425,6 +426,7 @@ def test_append_v3_fp8_random_weights(T):
     ("fp32", "bf16", 0, 1, 300),
     ("bf16", "bf16", 0, 0, 5),     # no tokens: the query half alone
     ("fp8", "bf16", 0, 7, 0),      # no query rows: the append half alone
+    ("fp8p2", "bf16", 0, 33, 70),  # power-of-two tile scales
     ("fp32", "fp32", 0, 5, 3),     # VALU forms, two launches
     ("bf16", "bf16", 1, 9, 9),     # VALU query form beside the matrix-core append
 ])
@@ -437,7 +439,7 @@ def test_append_query_absorb_one_call_matches_two_calls(cache_dtype, act, flags,
     cfg = dataclasses.replace(W.CONFIGS["v3"], cache_dtype=cache_dtype, act_dtype=act)
     dims = dims_of(cfg, flags)
     adt = torch.bfloat16 if act == "bf16" else torch.float32
-    cdt = {"bf16": torch.bfloat16, "fp32": torch.float32, "fp8": torch.uint8}[cache_dtype]
+    cdt = {"bf16": torch.bfloat16, "fp32": torch.float32, "fp8": torch.uint8, "fp8p2": torch.uint8}[cache_dtype]
     h = W.normal((T, d.d_model), 70 + T, device="cuda").to(adt)
     w_dkv = W.weight(d.d_latent, d.d_model, 71, dtype=adt, device="cuda")
     w_kr = W.weight(d.d_rope, d.d_model, 72, dtype=adt, device="cuda")
@@ -454,7 +456,7 @@ def test_append_query_absorb_one_call_matches_two_calls(cache_dtype, act, flags,
 
     def run(one_call):
         cache = torch.zeros((nblk, 64, d.row), dtype=cdt, device="cuda")
-        scales = torch.zeros((nblk, 64, 5), device="cuda") if cache_dtype == "fp8" else None
+        scales = torch.zeros((nblk, 64, 5), device="cuda") if cache_dtype in FP8 else None
         q_out = torch.full((rows, d.num_heads, d.row), float("nan"), dtype=adt, device="cuda")
         if one_call:
             M.mla_cache_append_query_absorb(dims, h, w_dkv, w_kr, seq_ids, positions, table_t, cache, scales,
@@ -564,14 +566,16 @@ def _ragged_sample(case, n=16):
 
 
 FULL = {"v3": lambda c: list(range(64)), "long": lambda c: [0, 1, 2, 3],
-        "fp8": lambda c: list(range(0, 128, 4)), "ragged": _ragged_sample}
+        "fp8": lambda c: list(range(0, 128, 4)), "fp8p2": lambda c: list(range(1, 128, 4)),
+        "ragged": _ragged_sample}
 
 
 @pytest.mark.parametrize("name", sorted(FULL))
 def test_full_size(name):
     """Every config at its full size in the default launch configuration:
-    all sequences of v3 and long, 32 of fp8, and 17 of ragged (lengths from
-    the shortest to the longest, the 2.29 GB pool's last block included)."""
+    all sequences of v3 and long, 32 of fp8 (either scale format), and 17 of
+    ragged (lengths from the shortest to the longest, the 2.29 GB pool's last
+    block included)."""
     cfg = W.CONFIGS[name]
     case = DecodeCase(cfg)
     ids = FULL[name](case)
@@ -581,7 +585,7 @@ def test_full_size(name):
         hi = [b for b in ids if int(case.table[b].max()) * row_bytes >= TWO_GIB]
         assert hi, "no compared sequence reads past 2 GiB"
     u, lse = case.run()
-    if cfg.cache_dtype == "fp8":
+    if cfg.cache_dtype in FP8:
         compare_sampled(case, u, lse, ids, rel_bar=5e-2, abs_bar=None)
     else:
         compare_sampled(case, u, lse, ids)
