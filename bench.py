@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense, published
-BYTES_PER_KV_TOKEN = {"bf16": 1152, "fp8": 596, "fp32": 2304}
+BYTES_PER_KV_TOKEN = {"bf16": 1152, "fp8": 596, "fp8p2": 596, "fp32": 2304}
 
 
 def parse():
@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="v3", choices=["v3", "long", "ragged", "fp8"])
+    p.add_argument("--workload", default="v3", choices=["v3", "long", "ragged", "fp8", "fp8p2"])
     p.add_argument("--partitions", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true",
@@ -119,24 +119,31 @@ def main():
     B, n_q = cfg.batch, cfg.n_q
     table, nblk = W.page_table(lens, bs, cfg.seed)
     kv_tokens = int(lens.sum())
-    cdt = {"bf16": M.BF16, "fp8": M.FP8_E4M3}[cfg.cache_dtype]
-    # the arithmetic type of the decode's matrix products: both caches are
-    # multiplied on bf16 MFMA (the fp8 cache is dequantised to bf16 in LDS)
-    compute_dtype = "bf16"
+    cdt = {"bf16": M.BF16, "fp8": M.FP8_E4M3, "fp8p2": M.FP8_E4M3_PO2}[cfg.cache_dtype]
+    fp8 = cfg.cache_dtype in ("fp8", "fp8p2")
+    # the arithmetic type of the decode's matrix products: bf16 MFMA for the
+    # bf16 cache and for the e4m3 cache with any tile scales (dequantised to
+    # bf16 in LDS); the power-of-two e4m3 cache takes its scores on fp8 MFMA
+    # and its output product on bf16 MFMA
+    compute_dtype = "fp8+bf16" if cfg.cache_dtype == "fp8p2" and not args.generic else "bf16"
     dims = M.make_dims(H, d.d_latent, d.d_rope, d.d_nope, d.d_v, bs, cdt, M.BF16,
                        flags=M.FLAG_GENERIC_DECODE if args.generic else 0)
 
     # ---- resident inputs -------------------------------------------------
-    elem = 1 if cfg.cache_dtype == "fp8" else 2
+    elem = 1 if fp8 else 2
     pool_bytes = nblk * bs * D * elem
     n_copies = max(2, math.ceil(1.0e9 / pool_bytes) + 1)
     pools, scales = [], []
     for i in range(n_copies):
         rows = W.cache_rows(nblk * bs, cfg, seed=cfg.seed + 10 + i, device=dev)
-        if cfg.cache_dtype == "fp8":
+        if fp8:
             # synthetic e4m3 bytes: the workload's rows reduced to codes by the
             # library's own cast; the benchmark times decode, not the codec
+            # (one scale per row, stored for each of its five tiles; a power
+            # of two for the power-of-two format)
             amax = rows.view(-1, D)[:, :].abs().amax(dim=1, keepdim=True).clamp_min(1e-6)
+            if cfg.cache_dtype == "fp8p2":
+                amax = torch.exp2(torch.ceil(torch.log2(amax / 448.0))) * 448.0
             sc = (amax / 448.0).expand(-1, 5).contiguous()
             pools.append((rows / amax * 448.0).clamp(-448, 448).to(torch.float8_e4m3fn)
                          .view(torch.uint8).view(nblk, bs, D))
@@ -261,12 +268,18 @@ def main():
     # t_roof = max(bytes / HBM peak, flops / MFMA peak of the arithmetic dtype):
     # whichever is larger bounds the kernel and is the one reported.
     bytes_alg = kv_tokens * BYTES_PER_KV_TOKEN[cfg.cache_dtype] + B * n_q * H * D * 2
-    flops_alg = kv_tokens * n_q * 2 * H * (D + d.d_latent)
+    flops_qk = kv_tokens * n_q * 2 * H * D
+    flops_pv = kv_tokens * n_q * 2 * H * d.d_latent
+    flops_alg = flops_qk + flops_pv
     achieved_gbps = bytes_alg / (decode_ms * 1e-3) / 1e9
     achieved_tflops = flops_alg / (decode_ms * 1e-3) / 1e12
-    mfma_peak = MFMA_PEAK_TFLOPS[compute_dtype]
     t_hbm = bytes_alg / (HBM_PEAK_GBPS * 1e9)
-    t_mfma = flops_alg / (mfma_peak * 1e12)
+    if compute_dtype == "fp8+bf16":   # scores at the fp8 peak, the output product at the bf16 peak
+        t_mfma = (flops_qk / MFMA_PEAK_TFLOPS["fp8"] + flops_pv / MFMA_PEAK_TFLOPS["bf16"]) / 1e12
+        mfma_peak = round(flops_alg / t_mfma / 1e12, 1)   # the mix's effective peak
+    else:
+        mfma_peak = MFMA_PEAK_TFLOPS[compute_dtype]
+        t_mfma = flops_alg / (mfma_peak * 1e12)
     kernel_src = "decode_generic.hip" if args.generic else "decode_mfma.hip"
     traffic = traffic_from_profile(kernel_src, args.workload)
     if t_hbm >= t_mfma:
@@ -409,13 +422,13 @@ def cpu_baseline(cfg, pool, sc, table, lens, q_in, w_uk, h, w_dkv, w_kr, w_uv, s
     bs = d.block_size
     n_seq = 4
     ids = list(range(n_seq))
-    host_pool = {"dtype": cfg.cache_dtype}
+    host_pool = {"dtype": "fp8" if cfg.cache_dtype in ("fp8", "fp8p2") else cfg.cache_dtype}
     blocks = np.unique(table[ids][table[ids] >= 0])
     data = np.zeros((pool.shape[0],) + tuple(pool.shape[1:]),
-                    dtype=np.uint8 if cfg.cache_dtype == "fp8" else np.uint16)
+                    dtype=np.uint8 if host_pool["dtype"] == "fp8" else np.uint16)
     idx = torch.from_numpy(blocks.astype(np.int64)).to(pool.device)
     raw = pool.index_select(0, idx).cpu()
-    data[blocks] = raw.numpy() if cfg.cache_dtype == "fp8" else raw.view(torch.int16).numpy().view(np.uint16)
+    data[blocks] = raw.numpy() if host_pool["dtype"] == "fp8" else raw.view(torch.int16).numpy().view(np.uint16)
     host_pool["data"] = data
     if sc is not None:
         s = np.zeros((pool.shape[0], bs, 5), np.float32)

@@ -60,7 +60,7 @@ MLA_DEV void load_w_rows(unsigned char* dst, const void* w_uv, int h, int dv, in
   for (int i = 0; i < per; ++i) {
     const int row = wave * per + i;
     const uint32_t voff = uint32_t((lane ^ (row & 15)) << 4);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+    asm volatile(MLA_ASM_VMEM_WAIT "buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
                  : "v"(voff), "s"(rs), "s"(row * kRowBytes), "{m0}"(lds_addr(dst + row * kRowBytes))
                  : "memory");

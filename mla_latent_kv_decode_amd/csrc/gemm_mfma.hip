@@ -153,7 +153,7 @@ MLA_DEV void tile_to_lds(unsigned char* dst, const unsigned char* src, int nrows
     const int row = 2 * i + (lane >> 5);
     // lane fills LDS chunk slot lane & 31 of its row with source chunk (lane & 31) ^ (row & 31)
     const uint32_t voff = uint32_t(row * row_stride + (((lane & 31) ^ (row & 31)) << 4));
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile(MLA_ASM_VMEM_WAIT "buffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(r), "{m0}"(lds_addr_u8(dst + i * 1024))
                  : "memory");

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kNT, 4 / kCB) void linear_mfma_kernel(LinearArgs a,
     for (int i = 0; i < kCols / kWaves; ++i) {
       const int r = wave * (kCols / kWaves) + i;
       const uint32_t voff = uint32_t(r * K * 2 + k0 * 2 + ((lane ^ (r & 31)) << 4));
-      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+      asm volatile(MLA_ASM_VMEM_WAIT "buffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
                    : "v"(voff), "s"(rs), "{m0}"(lds_addr(wt + r * kRowB))
                    : "memory");

@@ -9,6 +9,15 @@
 #define MLA_DEV static __device__ __forceinline__
 #define MLA_HD __host__ __device__ __forceinline__
 
+// Wait states in front of every buffer load issued from inline asm.  The
+// compiler resolves hardware hazards only for instructions it can see, so
+// an asm load must cover the ones its operands can meet: an SGPR operand
+// (soffset, descriptor) written by a VALU instruction -- v_readfirstlane, or
+// a reload of a spilled SGPR with v_readlane -- needs 5 wait states before
+// a VMEM instruction reads it, and a write of M0 needs 1 before an LDS DMA
+// uses it.
+#define MLA_ASM_VMEM_WAIT "s_nop 4\n\t"
+
 namespace mla {
 
 constexpr int kWave = 64;
@@ -266,7 +275,7 @@ MLA_DEV void lens_window_issue(const LdsLensWindow& w, int c) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(w.g + c), (short)0, min(w.B - c, 256) * 4, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+    asm volatile(MLA_ASM_VMEM_WAIT "buffer_load_dword %0, %1, %2 offen lds"
                  :
                  : "v"(int(threadIdx.x) * 4), "s"(r), "s"(i * 256), "{m0}"(w.lds + i * 256)
                  : "memory");

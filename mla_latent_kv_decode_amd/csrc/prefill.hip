@@ -96,7 +96,7 @@ MLA_DEV void o_ready(f32x16 (&O)[4]) {
 // One 1 KB direct load into LDS: 8 rows of 8 chunks of 16 bytes; lane l
 // fills slot l % 8 of row l / 8 with the row's chunk (l % 8) ^ swz(t).
 MLA_DEV void load_sub(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile(MLA_ASM_VMEM_WAIT "buffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(r), "s"(soff), "{m0}"(lds)
                : "memory");

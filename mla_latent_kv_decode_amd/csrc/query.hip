@@ -121,7 +121,7 @@ MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
     for (int i = wave; i < dn / 4; i += kNT / kWave) {
       const int n = 4 * i + (lane >> 4), c = lane & 15;
       const uint32_t voff = uint32_t(n * kDL * 2 + ((c ^ wswz(n)) << 4));
-      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+      asm volatile(MLA_ASM_VMEM_WAIT "buffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
                    : "v"(voff), "s"(rs), "{m0}"(lds_addr(w_lds + i * 1024))
                    : "memory");
