@@ -18,7 +18,9 @@ are rotated so the 256 MB last-level cache cannot serve the cache stream.
 The timed region launches the calls of a step with only a start and a
 stop event (--graph replays one captured HIP graph per step instead); the
 per-kernel times, and the decode time the roofline uses, come from a second
-pass of the same steps with an event around every call.
+pass of the same steps with an event around every call.  Outside the
+timed step, the dense layers around it (mla_linear) and chunked prefill over
+the latent cache (mla_prefill) are timed on their own.
 
 Prints one JSON line (rank 0).  Metric: KV-tokens/s = sum_b L_b per step / time.
 """
@@ -52,6 +54,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true",
                    help="skip the separate timing of the query projections and W^O (mla_linear)")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the separate timing of chunked prefill over the latent cache (mla_prefill)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--generic", action="store_true", help="force the generic decode kernel")
     p.add_argument("--separate", action="store_true",
@@ -302,6 +306,7 @@ def main():
 
     # ---- the dense layers around the step (outside the timed region) -------
     dense = None if args.no_dense else dense_layers(M, W, dims, d, B * n_q, args.steps, stream)
+    prefill = None if args.no_prefill else prefill_chunks(M, W, stream)
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None
@@ -337,6 +342,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "dense_layers": dense,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -375,6 +381,52 @@ def dense_layers(M, W, dims, d, rows, steps, stream):
         out[name] = {"n": n, "k": k, "ms": round(ms, 5), "weight_gbps": round(gbps, 1),
                      "frac": round(gbps / HBM_PEAK_GBPS, 4)}
         del ws, x, y, wsp
+    return out
+
+
+PREFILL_CHUNKS = ((8192, 1024), (16384, 2048))
+
+
+def prefill_chunks(M, W, stream, iters=30):
+    """Chunked prefill over the latent cache (mla_prefill, bf16, DeepSeek-V3
+    dims), timed on its own at two (cached rows T, chunk C) shapes: the last C
+    of T rows are the chunk's own tokens.  Algorithmic flops per call: the
+    K^C and V expansions, 2 * T * d_c * H * (d_nope + d_v), plus the causal
+    attention, 2 * H * (d_nope + d_R + d_v) per visible (query, key) pair,
+    sum_j (T - C + j + 1) pairs; against the dense bf16 matrix-core peak."""
+    import torch
+    cfg = W.CONFIGS["v3"]
+    d = cfg.dims
+    H, bs = d.num_heads, d.block_size
+    dims = M.make_dims(H, d.d_latent, d.d_rope, d.d_nope, d.d_v, bs, M.BF16, M.BF16)
+    std = 1 / math.sqrt(d.d_latent)
+    w_uk = W.normal((H, d.d_nope, d.d_latent), 601, std=std, device="cuda").to(torch.bfloat16)
+    w_uv = W.normal((H, d.d_v, d.d_latent), 602, std=std, device="cuda").to(torch.bfloat16)
+    out = {"iters": iters, "dtype": "bf16"}
+    for i, (T, C) in enumerate(PREFILL_CHUNKS):
+        lens = np.array([T], np.int32)
+        table, nblk = W.page_table(lens, bs, 610 + i)
+        pool = W.cache_rows(nblk * bs, cfg, seed=620 + i, device="cuda").to(torch.bfloat16).view(nblk, bs, d.row)
+        tab = torch.from_numpy(table[0]).cuda()
+        q = W.normal((C, H, d.d_nope + d.d_rope), 630 + i, device="cuda").to(torch.bfloat16)
+        y = torch.empty(C, H, d.d_v, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(M.mla_prefill_workspace_size(dims, C, T), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            M.mla_prefill(dims, q, pool, tab, T, w_uk, w_uv, y, ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            M.mla_prefill(dims, q, pool, tab, T, w_uk, w_uv, y, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        pairs = C * (T - C) + C * (C + 1) // 2
+        flops = 2 * T * d.d_latent * H * (d.d_nope + d.d_v) + 2 * H * (d.d_nope + d.d_rope + d.d_v) * pairs
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"T{T}_C{C}"] = {"cached_rows": T, "chunk": C, "ms": round(ms, 5), "flops": flops,
+                             "tflops": round(tf, 1), "frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4)}
+        del pool, q, y, ws
     return out
 
 
