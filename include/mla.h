@@ -322,7 +322,8 @@ int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
  *   workspace      mla_prefill_workspace_size(dims, n_tokens, seq_len) bytes,
  *                  256-byte aligned: the gathered latents and the expanded keys
  *                  and values ((d_latent + d_rope + 2 * 128 * num_heads) * 2
- *                  bytes per cached token) plus scratch
+ *                  bytes per cached token) and the rotated queries
+ *                  (n_tokens * num_heads * (d_nope + d_rope) * 2 bytes)
  * Supported: bf16 activations and cache with the DeepSeek-V3 dimensions
  * (H = 128, d_latent = 512, d_rope = 64, d_nope = d_v = 128); other dims
  * return MLA_ERR_UNSUPPORTED (the workspace size is 0).  fp32 accumulation,

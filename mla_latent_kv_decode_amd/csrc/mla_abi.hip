@@ -606,7 +606,7 @@ namespace {
 // expanded content keys and values [T][H * d_nope], [T][H * d_v] (act dtype),
 // then the expansion's linear-layer scratch.
 struct PrefillLayout {
-  size_t kr_off, kc_off, v_off, q_off, lin_off, lin_bytes, total;
+  size_t kr_off, kc_off, v_off, q_off, total;
 };
 PrefillLayout prefill_layout(const mla_dims* d, int n_tokens, int seq_len) {
   PrefillLayout w;
@@ -615,17 +615,7 @@ PrefillLayout prefill_layout(const mla_dims* d, int n_tokens, int seq_len) {
   w.kc_off = align_up(w.kr_off + T * d->d_rope * e, 256);
   w.v_off = align_up(w.kc_off + T * size_t(d->num_heads) * d->d_nope * e, 256);
   w.q_off = align_up(w.v_off + T * size_t(d->num_heads) * d->d_v * e, 256);
-  w.lin_off = align_up(w.q_off + size_t(n_tokens) * d->num_heads * (d->d_nope + d->d_rope) * e, 256);
-  mla::LinearArgs la{};
-  la.rows = seq_len;
-  la.k = d->d_latent;
-  la.act_dtype = MLA_BF16;
-  la.n = d->num_heads * d->d_nope;
-  size_t lin = mla::linear_mfma_workspace(la);
-  la.n = d->num_heads * d->d_v;
-  lin = std::max(lin, mla::linear_mfma_workspace(la));
-  w.lin_bytes = lin;
-  w.total = align_up(w.lin_off + lin, 256);
+  w.total = align_up(w.q_off + size_t(n_tokens) * d->num_heads * (d->d_nope + d->d_rope) * e, 256);
   return w;
 }
 bool prefill_dims_ok(const mla_dims* d) {
@@ -668,6 +658,8 @@ int mla_prefill(const mla_dims* d, const void* q_in, int32_t n_tokens, const voi
   a.ws_kc = ws + w.kc_off;
   a.ws_v = ws + w.v_off;
   a.ws_q = ws + w.q_off;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
   a.out = out;
   a.n_tokens = n_tokens;
   a.seq_len = seq_len;
@@ -681,19 +673,10 @@ int mla_prefill(const mla_dims* d, const void* q_in, int32_t n_tokens, const voi
   a.rope_base = d->rope_base > 0.f ? d->rope_base : 10000.f;
   if (!mla::prefill_supported(a)) return fail(MLA_ERR_INVALID_ARGUMENT, "prefill: misaligned pointer");
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // gather + q rotation, the expansion K^C = c W^UK^T and V = c W^UV^T
+  // (W^UK, W^UV: [H][128][d_c] = [H*128][d_c]), then attention
   hipError_t e = mla::launch_prefill_gather(a, st);
-  // the expansion: K^C = c W^UK^T and V = c W^UV^T (W^UK, W^UV: [H][128][d_c] = [H*128][d_c])
-  for (int m = 0; m < 2 && e == hipSuccess; ++m) {
-    mla::LinearArgs la{};
-    la.x = a.ws_c;
-    la.w = m == 0 ? w_uk : w_uv;
-    la.y = ws + (m == 0 ? w.kc_off : w.v_off);
-    la.rows = seq_len;
-    la.n = d->num_heads * (m == 0 ? d->d_nope : d->d_v);
-    la.k = d->d_latent;
-    la.act_dtype = MLA_BF16;
-    e = mla::launch_linear_mfma(la, ws + w.lin_off, st);
-  }
+  if (e == hipSuccess) e = mla::launch_prefill_expand(a, st);
   if (e == hipSuccess) e = mla::launch_prefill_attn(a, st);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

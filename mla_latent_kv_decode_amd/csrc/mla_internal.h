@@ -117,8 +117,10 @@ struct PrefillArgs {
   const int32_t* page_table; // the sequence's row
   void* ws_c;                // [T][d_latent] gathered latents
   void* ws_kr;               // [T][d_rope] gathered RoPE keys
-  const void* ws_kc;         // [T][H * d_nope] expanded content keys
-  const void* ws_v;          // [T][H * d_v] expanded values
+  void* ws_kc;               // [T][H * d_nope] expanded content keys
+  void* ws_v;                // [T][H * d_v] expanded values
+  const void* w_uk;          // [H][d_nope][d_latent] bf16 = [H * d_nope][d_latent]
+  const void* w_uv;          // [H][d_v][d_latent] bf16 = [H * d_v][d_latent]
   void* ws_q;                // [C][H][d_nope + d_rope] the queries, q^R rotated
   void* out;                 // [C][H][d_v] bf16
   int n_tokens, seq_len, block_size, H, d_latent, d_rope, d_nope, d_v;
@@ -126,6 +128,7 @@ struct PrefillArgs {
 };
 bool prefill_supported(const PrefillArgs& a);
 hipError_t launch_prefill_gather(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_expand(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t st);
 
 bool decode_generic_supported(const DecodeArgs& a);

@@ -102,37 +102,50 @@ MLA_DEV void load_sub(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff
                : "memory");
 }
 
-MLA_DEV void rope_pair(float x, float z, int pos, double inv_freq, float* y0, float* y1) {
-  double sd, cd;
-  sincos(double(pos) * inv_freq, &sd, &cd);
-  const float cs = float(cd), sn = float(sd);
-  *y0 = x * cs - z * sn;
-  *y1 = z * cs + x * sn;
-}
-
 // The chunk's queries with q^R rotated at each token's position (rotate-half
 // pairs (j, j + 32), angle pos * base^(-j/32) in fp64, cos/sin rounded to
-// fp32): one thread per (token, head, pair); q^C is copied through.
+// fp32).  One workgroup per chunk token: the 32 angles are computed once and
+// shared by the token's 128 heads through LDS; one thread per (head, 16-byte
+// piece): q^C pieces are copied, q^R pieces (8 pairs: chunk c with chunk
+// c + 4) are rotated.
 __global__ __launch_bounds__(kNT) void prefill_rope_kernel(PrefillArgs a) {
-  const int64_t i = int64_t(blockIdx.x) * kNT + threadIdx.x;
-  if (i >= int64_t(a.n_tokens) * kH * (kDR / 2 + kDN / 2)) return;
-  const int per = kDR / 2 + kDN / 2;  // 32 RoPE pairs + 64 pairs of q^C channels per head
-  const int64_t row = i / per;        // token * H + head
-  const int k = int(i % per);
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const __bf16*>(a.q) + row * kDK);
-  uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.ws_q) + row * kDK);
-  if (k < kDN / 2) {  // two q^C channels
-    dst[k] = src[k];
-    return;
+  __shared__ float cs[kDR / 2], sn[kDR / 2];
+  const int tok = blockIdx.x;
+  const int pos = a.seq_len - a.n_tokens + tok;
+  if (threadIdx.x < kDR / 2) {
+    const int j = threadIdx.x;
+    double sd, cd;
+    sincos(double(pos) * pow(double(a.rope_base), -double(j) / double(kDR / 2)), &sd, &cd);
+    cs[j] = float(cd);
+    sn[j] = float(sd);
   }
-  const int j = k - kDN / 2;
-  const __bf16* q = static_cast<const __bf16*>(a.q) + row * kDK + kDN;
-  __bf16* o = static_cast<__bf16*>(a.ws_q) + row * kDK + kDN;
-  const int pos = a.seq_len - a.n_tokens + int(row / kH);
-  float y0, y1;
-  rope_pair(float(q[j]), float(q[j + kDR / 2]), pos, pow(double(a.rope_base), -double(j) / double(kDR / 2)), &y0, &y1);
-  o[j] = (__bf16)y0;
-  o[j + kDR / 2] = (__bf16)y1;
+  __syncthreads();
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.q) + int64_t(tok) * kH * kDK);
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<__bf16*>(a.ws_q) + int64_t(tok) * kH * kDK);
+  constexpr int kPieces = kDN / 8 + kDR / 16;  // 16 q^C pieces + 4 q^R piece pairs per head
+  for (int i = threadIdx.x; i < kH * kPieces; i += kNT) {
+    const int h = i / kPieces, k = i % kPieces;
+    const int row = h * (kDK / 8);  // 24 pieces of 16 bytes per head
+    if (k < kDN / 8) {
+      dst[row + k] = src[row + k];
+      continue;
+    }
+    const int c = k - kDN / 8;      // q^R pieces c and c + 4: pairs (8c + e, 8c + e + 32)
+    const uint4 lo = src[row + kDN / 8 + c], hi = src[row + kDN / 8 + c + 4];
+    const __bf16* x = reinterpret_cast<const __bf16*>(&lo);
+    const __bf16* z = reinterpret_cast<const __bf16*>(&hi);
+    uint4 olo, ohi;
+    __bf16* y0 = reinterpret_cast<__bf16*>(&olo);
+    __bf16* y1 = reinterpret_cast<__bf16*>(&ohi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xv = float(x[e]), zv = float(z[e]), c_ = cs[8 * c + e], s_ = sn[8 * c + e];
+      y0[e] = (__bf16)(xv * c_ - zv * s_);
+      y1[e] = (__bf16)(zv * c_ + xv * s_);
+    }
+    dst[row + kDN / 8 + c] = olo;
+    dst[row + kDN / 8 + c + 4] = ohi;
+  }
 }
 
 __global__ __launch_bounds__(kNT) void prefill_gather_kernel(PrefillArgs a) {
@@ -150,6 +163,196 @@ __global__ __launch_bounds__(kNT) void prefill_gather_kernel(PrefillArgs a) {
     reinterpret_cast<uint4*>(a.ws_kr)[int64_t(t) * 8 + (k - 64)] = v;
 }
 
+// The expansion, Y = c . W^T for W = W^UK (Y = K^C) and W = W^UV (Y = V),
+// W viewed as [H*128][512]: a GEMM of T x 16384 outputs over a 512-deep
+// reduction, both operands contiguous along it.  One launch covers both
+// matrices.  A workgroup of eight waves computes a tile of 256 weight rows x
+// 256 tokens; each wave owns 128 x 64 (4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16, weight rows as the MFMA's rows so that a lane's
+// outputs are 4 consecutive columns of one token's row).  The reduction runs
+// in 8 stages of 64 (128 bytes of every row: whole cache lines, which halves
+// the requests in flight per byte against 64-byte pieces).  A stage (64 KB)
+// is loaded into registers one stage ahead and written to one of two LDS
+// buffers, rows swizzled by 16-byte piece so the fragment reads hit
+// distinct banks.  The workgroups are persistent, one per compute unit: the
+// next tile's first stage loads while a tile's outputs are written.  Tiles
+// are assigned so that each XCD keeps its own token tiles (in its L2) and
+// walks the weight tiles, its workgroups sharing one weight tile at a time.
+constexpr int kENT = 512;                                  // eight waves
+constexpr int kEN = 256;                                   // weight rows per tile
+constexpr int kET = 256;                                   // tokens per tile
+constexpr int kEK = 64;                                    // reduction per stage
+constexpr int kERowBytes = kEK * 2;                        // 128 bytes of a row per stage
+constexpr int kEStageBytes = (kEN + kET) * kERowBytes;     // 65536
+constexpr int kEChunks = kDC / kEK;                        // 8
+constexpr int kELoads = (kEN + kET) / 8;                   // 64 loads of 8 rows per stage
+constexpr int kELoadsPerWave = kELoads / (kENT / kWave);   // 8
+constexpr int kEWTiles = kH * kDN / kEN;                   // 64 weight tiles per matrix
+constexpr int kEOutRow = kDN * 2 + 16;                     // epilogue row in LDS (padded)
+constexpr int kELds = 2 * kEStageBytes > (kENT / kWave) * 64 * kEOutRow ? 2 * kEStageBytes
+                                                                       : (kENT / kWave) * 64 * kEOutRow;
+static_assert(kDN == kDV && kELoads % (kENT / kWave) == 0 && (kEN / 8) % kELoadsPerWave == 0 && kEChunks % 2 == 0,
+              "expansion tiling: a wave's loads are all weight rows or all token rows");
+
+// 16-byte piece p of row r of a stage sits in slot p ^ ((r >> 1) & 7)
+MLA_DEV int exp_slot(int r, int p) { return p ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(kENT, 1) void prefill_expand_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(128))) unsigned char smem[];
+  const int T = a.seq_len;
+  const int ntt = (T + kET - 1) / kET;
+  // persistent: the workgroups of one XCD (blockIdx % 8) walk that XCD's
+  // tiles in order, r = wt * ns + s for weight tile wt and the XCD's token
+  // tile s (token tiles xcd, xcd + 8, ...)
+  const int xcd = blockIdx.x % 8, wg = blockIdx.x / 8, nwg = gridDim.x / 8;
+  const int ns = (ntt - xcd + 7) / 8;
+  const int ntiles = 2 * kEWTiles * ns;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wn = wave & 1, wtk = wave >> 1;
+  const bool w_loads = wave * kELoadsPerWave < kEN / 8;  // wave-uniform: the wave loads weight rows
+  // the wave's rows: stage rows srow0 .. srow0 + 63; lane l takes row l / 8 of
+  // each group of 8, piece l % 8 (8 lanes read one row's 128 contiguous bytes)
+  const int srow0 = wave * kELoadsPerWave * 8;
+  const int lrow = lane >> 3, lpiece = lane & 7;
+  const int voff0 = ((w_loads ? srow0 : srow0 - kEN) + lrow) * (kDC * 2) + lpiece * 16;
+  // fragment reads: lane (g, i) takes row i of a 32-row block, piece 2 ks + g
+  const int fr = lane & 31, fg = lane >> 5;
+  uint32_t cofs[kEK / 16];
+#pragma unroll
+  for (int ks = 0; ks < kEK / 16; ++ks) cofs[ks] = uint32_t(fr * kERowBytes + exp_slot(fr, 2 * ks + fg) * 16);
+
+  struct Tile {
+    int m, n0, t0;
+    __amdgpu_buffer_rsrc_t rsrc;  // this wave's operand: weight rows or token rows
+  };
+  auto tile_of = [&](int r) __attribute__((always_inline)) {
+    Tile t;
+    const int wt = r / ns;
+    t.m = wt / kEWTiles;
+    t.n0 = (wt % kEWTiles) * kEN;
+    t.t0 = (xcd + 8 * (r % ns)) * kET;
+    if (w_loads) {
+      const unsigned char* wbase =
+          static_cast<const unsigned char*>(t.m == 0 ? a.w_uk : a.w_uv) + int64_t(t.n0) * kDC * 2;
+      t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, kEN * kDC * 2, 0x00020000);
+    } else {
+      // token rows past T lie outside the descriptor and load as zeros
+      const unsigned char* xbase = static_cast<const unsigned char*>(a.ws_c) + int64_t(t.t0) * kDC * 2;
+      t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)xbase, (short)0, min(kET, T - t.t0) * kDC * 2, 0x00020000);
+    }
+    return t;
+  };
+  auto fetch = [&](const Tile& t, int kc, u32x4 (&R)[kELoadsPerWave]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mm = 0; mm < kELoadsPerWave; ++mm)
+      R[mm] = __builtin_amdgcn_raw_buffer_load_b128(t.rsrc, voff0 + mm * 8 * (kDC * 2), kc * kERowBytes, 0);
+  };
+  auto put = [&](int kc, const u32x4 (&R)[kELoadsPerWave]) __attribute__((always_inline)) {
+    unsigned char* buf = smem + (kc & 1) * kEStageBytes;
+#pragma unroll
+    for (int mm = 0; mm < kELoadsPerWave; ++mm) {
+      const int row = srow0 + mm * 8 + lrow;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          (lds_u8*)(buf + row * kERowBytes + exp_slot(row, lpiece) * 16)) = R[mm];
+    }
+  };
+  f32x16 acc[4][2];
+  // the fragments of k step ks + 1 are read while the MFMAs of step ks run
+  // (two fragment sets, 48 registers; the scheduling barriers keep the
+  // compiler from hoisting more reads, which the 256-register budget of two
+  // waves per SIMD cannot hold next to the 128 accumulators)
+  auto compute = [&](int kc) __attribute__((always_inline)) {
+    const uint32_t base = lds_addr(smem) + uint32_t((kc & 1) * kEStageBytes);
+    bf16x8 af[2][4], bf[2][2];
+    auto read = [&](int ks, int j) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        af[j][nb] = lds_b128_at(base + uint32_t((wn * 128 + nb * 32) * kERowBytes) + cofs[ks]);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        bf[j][tb] = lds_b128_at(base + uint32_t((kEN + wtk * 64 + tb * 32) * kERowBytes) + cofs[ks]);
+    };
+    read(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kEK / 16; ++ks) {
+      if (ks + 1 < kEK / 16) read(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][nb], bf[ks & 1][tb], acc[nb][tb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (wg >= ntiles) return;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x4 R[kELoadsPerWave];
+  Tile cur = tile_of(wg);
+  fetch(cur, 0, R);
+  for (int r = wg; r < ntiles; r += nwg) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) acc[nb][tb] = f32x16{};
+    // stage s is fetched into registers one stage ahead and written to LDS
+    // buffer s & 1, which the barrier after the computation of stage s - 1
+    // (or after the previous tile's epilogue) freed
+    put(0, R);
+    fetch(cur, 1, R);
+    __syncthreads();
+    for (int kc = 0; kc < kEChunks; ++kc) {
+      compute(kc);
+      if (kc + 1 < kEChunks) {
+        put(kc + 1, R);
+        if (kc + 2 < kEChunks) fetch(cur, kc + 2, R);
+      }
+      __syncthreads();
+    }
+    // Epilogue.  Lane (g, i) holds weight rows 8 (q / 4) + 4 g + q % 4 of
+    // block nb, token i of block tb; a wave's 128 weight rows are one head's,
+    // and Y is head-major, [H][T][128], so the wave's 64 tokens are one
+    // contiguous 16 KB run.  The tile goes through LDS (rows padded against
+    // bank conflicts) and leaves as whole 1 KB pieces with non-temporal
+    // stores, which keep the operand tiles in L2.
+    unsigned char* stage = smem + wave * 64 * kEOutRow;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 v = {pack_bf16x2(acc[nb][tb][4 * q + 0], acc[nb][tb][4 * q + 1]),
+                           pack_bf16x2(acc[nb][tb][4 * q + 2], acc[nb][tb][4 * q + 3])};
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+              (lds_u8*)(stage + (tb * 32 + fr) * kEOutRow + (nb * 32 + 8 * q + 4 * fg) * 2)) = v;
+        }
+    // the next tile's first stage loads while this tile's outputs leave
+    const Tile nxt = tile_of(r + nwg < ntiles ? r + nwg : r);
+    if (r + nwg < ntiles) fetch(nxt, 0, R);
+    // lane l stores piece l % 16 of rows 4 i + l / 16; the lane's offsets are
+    // made opaque per tile so the compiler keeps them out of the main loop
+    int er = lane >> 4, ec = lane & 15;
+    asm volatile("" : "+v"(er), "+v"(ec));
+    const int head = (cur.n0 >> 7) + wn;
+    unsigned char* y = static_cast<unsigned char*>(cur.m == 0 ? a.ws_kc : a.ws_v) +
+                       (int64_t(head) * T + cur.t0 + wtk * 64) * (kDN * 2) + (er * (kDN * 2) + ec * 16);
+    const unsigned char* src = stage + er * kEOutRow + ec * 16;
+    const int lim = min(64, T - cur.t0 - wtk * 64) - er;  // rows 4 i + er < nrows
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (4 * i < lim) {
+        const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(
+            (const lds_u8*)(src + 4 * i * kEOutRow));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y + 4 * i * (kDN * 2)));
+      }
+    }
+    __syncthreads();  // the staging rows are read before the next tile's stage 0 lands
+    cur = nxt;
+  }
+}
+
 __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(128))) unsigned char smem[];
   const int lane = threadIdx.x % kWave;
@@ -163,6 +366,9 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
   const int C = a.n_tokens, T = a.seq_len, p0 = T - C;
   const int q_row = qb * kRowsPerWG + wave * 32 + hl;       // this lane's chunk token
   const int q_lim = p0 + min(q_row, C - 1);                 // last position it sees
+  // keys up to here are visible to every query of the wave: steps that end
+  // there need no causal mask
+  const int wave_vis = p0 + min(qb * kRowsPerWG + wave * 32, C - 1);
   // the workgroup's last token sees positions up to p0 + last row
   const int t_end = p0 + min(C, (qb + 1) * kRowsPerWG);     // positions [0, t_end)
   const int nsteps = (t_end + kStep - 1) / kStep;
@@ -180,19 +386,20 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
 
   // ---- loads of one step: 12 key sub-blocks (3 column groups: K^C, K^C, k^R)
   // and 8 value sub-blocks per step; wave w issues loads 5w .. 5w + 4 ----
-  const int64_t row_bytes = int64_t(kH) * kDN * 2;  // one token's K^C (or V) row of all heads
+  // K^C and V are head-major, [H][T][128]: a head's rows are contiguous
+  constexpr int row_bytes = kDN * 2;
+  const unsigned char* kc_head = static_cast<const unsigned char*>(a.ws_kc) + int64_t(h) * T * row_bytes;
+  const unsigned char* v_head = static_cast<const unsigned char*>(a.ws_v) + int64_t(h) * T * row_bytes;
   auto issue_step = [&](int s) __attribute__((always_inline)) {
     const int t0 = s * kStep;
     const int nvalid = min(kStep, T - t0);
     unsigned char* buf = smem + (s % kNBuf) * kBufBytes;
-    const unsigned char* kc = static_cast<const unsigned char*>(a.ws_kc) + int64_t(t0) * row_bytes + h * kDN * 2;
-    const unsigned char* vv = static_cast<const unsigned char*>(a.ws_v) + int64_t(t0) * row_bytes + h * kDV * 2;
+    const unsigned char* kc = kc_head + int64_t(t0) * row_bytes;
+    const unsigned char* vv = v_head + int64_t(t0) * row_bytes;
     const unsigned char* kr = static_cast<const unsigned char*>(a.ws_kr) + int64_t(t0) * kDR * 2;
     // descriptors cover the live rows only: rows past T read as zeros
-    const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0,
-        int(int64_t(nvalid - 1) * row_bytes + kDN * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vv, (short)0,
-        int(int64_t(nvalid - 1) * row_bytes + kDV * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, nvalid * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vv, (short)0, nvalid * row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rkr = __builtin_amdgcn_make_buffer_rsrc((void*)kr, (short)0, nvalid * kDR * 2, 0x00020000);
 #pragma unroll
     for (int m = 0; m < kLoadsPerWave; ++m) {
@@ -203,13 +410,13 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
         const int tg = k / 3, cg = k % 3;
         const uint32_t dst = lds_addr(buf) + uint32_t((tg * kKG + cg) * 1024);
         if (cg < 2)
-          load_sub(rkc, dst, int((t) * row_bytes) + chunk * 16, cg * 128);
+          load_sub(rkc, dst, t * row_bytes + chunk * 16, cg * 128);
         else
           load_sub(rkr, dst, t * kDR * 2 + chunk * 16, 0);
       } else {
         const int kk = k - 12, tg = kk / 2, cg = kk % 2;
         const uint32_t dst = lds_addr(buf) + uint32_t(kKBytes + (tg * kVG + cg) * 1024);
-        load_sub(rv, dst, int((t) * row_bytes) + chunk * 16, cg * 128);
+        load_sub(rv, dst, t * row_bytes + chunk * 16, cg * 128);
       }
     }
   };
@@ -271,9 +478,11 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
       if constexpr (kQKOn) {
         if (k == 0) {
           scores_ready(S);
-          const int lim = q_lim - (h_ * kStep + 4 * g);  // causal: token index <= q_lim
+          if (h_ * kStep + kStep - 1 > wave_vis) {  // wave-uniform
+            const int lim = q_lim - (h_ * kStep + 4 * g);  // causal: token index <= q_lim
 #pragma unroll
-          for (int r = 0; r < 16; ++r) S[r] = (8 * (r / 4) + (r % 4) > lim) ? -INFINITY : S[r];
+            for (int r = 0; r < 16; ++r) S[r] = (8 * (r / 4) + (r % 4) > lim) ? -INFINITY : S[r];
+          }
         }
         if (k >= 1 && k < 9) {
           const int i = (k - 1) >> 2, e = 2 * ((k - 1) & 3);
@@ -380,8 +589,20 @@ bool prefill_supported(const PrefillArgs& a) {
 hipError_t launch_prefill_gather(const PrefillArgs& a, hipStream_t st) {
   const int64_t n = int64_t(a.seq_len) * 72;
   hipLaunchKernelGGL(prefill_gather_kernel, dim3(unsigned((n + kNT - 1) / kNT)), dim3(kNT), 0, st, a);
-  const int64_t m = int64_t(a.n_tokens) * kH * (kDR / 2 + kDN / 2);
-  hipLaunchKernelGGL(prefill_rope_kernel, dim3(unsigned((m + kNT - 1) / kNT)), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL(prefill_rope_kernel, dim3(unsigned(a.n_tokens)), dim3(kNT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_expand(const PrefillArgs& a, hipStream_t st) {
+  const int smem = kELds;
+  if (hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(prefill_expand_kernel), smem); e != hipSuccess)
+    return e;
+  // one persistent workgroup per compute unit (the LDS allows no second),
+  // the same number on every XCD; never more than the tiles of an XCD need
+  const int ntt = (a.seq_len + kET - 1) / kET;
+  const int per_xcd_tiles = 2 * kEWTiles * ((ntt + 7) / 8);
+  const int per_xcd = std::max(1, std::min(mla_device_cu_count() / 8, per_xcd_tiles));
+  hipLaunchKernelGGL(prefill_expand_kernel, dim3(unsigned(8 * per_xcd)), dim3(kENT), smem, st, a);
   return hipGetLastError();
 }
 
