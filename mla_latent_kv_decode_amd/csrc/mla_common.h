@@ -150,6 +150,9 @@ MLA_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 MLA_DEV int tid_fresh() {
   int t = int(threadIdx.x);
   asm volatile("" : "+v"(t));
+  // (the asm hides the range too: restate it, so that % and / by powers of
+  // two stay single masks and shifts instead of signed sequences)
+  __builtin_assume(t >= 0 && t < 1024);
   return t;
 }
 MLA_DEV int64_t uniform64(int64_t v) {
