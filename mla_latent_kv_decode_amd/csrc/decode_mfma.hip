@@ -717,17 +717,20 @@ void decode_mfma_kernel(DecodeArgs a) {
       // chunks per lane (token hl, chunk 2 wave + g + 8 i of tile i),
       // interleaved with the output MFMAs below
       u32x4 cq;
+      // this lane's conversion offsets, once per step (not kept across steps)
+      uint32_t cv_rd = 0, cv_wr = 0;
+      if constexpr (kP2 && kQKOn) {  // (the step's own codes are converted whenever its scores run)
+        const int dl = tid_fresh() % kWave, dg = (2 * wave + dl / 32), dt = dl % 32;
+        cv_rd = lds_addr(cbuf(h % 3)) + uint32_t((dg >> 2) * 2048 + dt * 64 + (((dg & 3) ^ cswz(dt)) << 4));
+        cv_wr = lds_addr(vbuf(h & 1)) + uint32_t(v8_off(dt, 2 * dg));
+      }
       auto v_read = [&](int i) __attribute__((always_inline)) {
         typedef __attribute__((address_space(3))) const u32x4 lds_u4;
-        const int dl = tid_fresh() % kWave, dg = (2 * wave + dl / 32), dt = dl % 32;
-        const uint32_t addr = lds_addr(cbuf(h % 3)) + uint32_t((dg >> 2) * 2048 + i * 4096 + dt * 64 +
-                                                                (((dg & 3) ^ cswz(dt)) << 4));
-        cq = *(lds_u4*)(uintptr_t)addr;
+        cq = *(lds_u4*)(uintptr_t)(cv_rd + uint32_t(i * 4096));
       };
       auto v_write = [&](int i) __attribute__((always_inline)) {
         typedef __attribute__((address_space(3))) u32x4 lds_u4w;
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const int dl = tid_fresh() % kWave, dg = (2 * wave + dl / 32), dt = dl % 32;
         uint32_t o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -736,7 +739,7 @@ void decode_mfma_kernel(DecodeArgs a) {
           o[2 * e] = __builtin_bit_cast(uint32_t, lo);
           o[2 * e + 1] = __builtin_bit_cast(uint32_t, hi);
         }
-        const uint32_t addr = lds_addr(vbuf(h & 1)) + uint32_t(v8_off(dt, 2 * dg) + i * 2048);
+        const uint32_t addr = cv_wr + uint32_t(i * 2048);
         *(lds_u4w*)(uintptr_t)addr = u32x4{o[0], o[1], o[2], o[3]};
         *(lds_u4w*)(uintptr_t)(addr ^ 16u) = u32x4{o[4], o[5], o[6], o[7]};
       };
