@@ -110,15 +110,18 @@ def test_prefill_matches_oracle(T, C, heads):
     assert max_abs(got, ref) <= 2e-2, (T, C)
 
 
-def test_prefill_full_size_chunk():
-    """An 8192-token sequence whose last 1024 tokens are the chunk: sampled
-    heads against the oracle, every output finite."""
-    case = PrefillCase(8192, 1024, seed=77)
+@pytest.mark.parametrize("T,C,seed", [(8192, 1024, 77), (16384, 2048, 78), (3000, 3000, 79)])
+def test_prefill_full_size_chunk(T, C, seed):
+    """The benchmark's chunk shapes (the last C of T tokens) and a whole
+    3000-token prompt as one chunk: sampled heads against the oracle, every
+    output finite."""
+    case = PrefillCase(T, C, seed=seed)
     out = case.run()
     assert torch.isfinite(out).all()
-    ref = case.oracle([0, 77, 127])
-    got = to_f64(out)[:, [0, 77, 127]]
-    assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2
+    heads = [0, 77, 127]
+    ref = case.oracle(heads)
+    got = to_f64(out)[:, heads]
+    assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2, (T, C)
 
 
 def test_prefill_matches_absorbed_decode_on_gpu():
