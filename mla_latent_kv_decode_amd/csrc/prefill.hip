@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
   }
 
   // ---- loads of one step: 12 key sub-blocks (3 column groups: K^C, K^C, k^R)
-  // and 8 value sub-blocks per step; wave w issues loads 5w .. 5w + 4 ----
+  // and 8 value sub-blocks per step, five per wave ----
   // K^C and V are head-major, [H][T][128]: a head's rows are contiguous
   constexpr int row_bytes = kDN * 2;
   const unsigned char* kc_head = static_cast<const unsigned char*>(a.ws_kc) + int64_t(h) * T * row_bytes;
@@ -401,25 +401,20 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
     const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, nvalid * row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vv, (short)0, nvalid * row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rkr = __builtin_amdgcn_make_buffer_rsrc((void*)kr, (short)0, nvalid * kDR * 2, 0x00020000);
-#pragma unroll
-    for (int m = 0; m < kLoadsPerWave; ++m) {
-      const int k = wave * kLoadsPerWave + m;  // wave-uniform
-      const int t = (k < 12 ? (k / 3) : ((k - 12) / 2)) * 8 + lane / 8;  // token inside the step
-      const int slot = lane % 8, chunk = slot ^ swz(t);
-      if (k < 12) {
-        const int tg = k / 3, cg = k % 3;
-        const uint32_t dst = lds_addr(buf) + uint32_t((tg * kKG + cg) * 1024);
-        if (cg < 2)
-          load_sub(rkc, dst, t * row_bytes + chunk * 16, cg * 128);
-        else
-          load_sub(rkr, dst, t * kDR * 2 + chunk * 16, 0);
-      } else {
-        const int kk = k - 12, tg = kk / 2, cg = kk % 2;
-        const uint32_t dst = lds_addr(buf) + uint32_t(kKBytes + (tg * kVG + cg) * 1024);
-        load_sub(rv, dst, t * row_bytes + chunk * 16, cg * 128);
-      }
-    }
+    // wave w loads token group w (8 tokens) of every column group: K^C
+    // twice, k^R, V twice -- the same five loads in every wave, no branches
+    const int t = wave * 8 + lane / 8;  // token inside the step
+    const int chunk = (lane % 8) ^ swz(t);
+    const uint32_t kdst = lds_addr(buf) + uint32_t(wave * kKG * 1024);
+    const uint32_t vdst = lds_addr(buf) + uint32_t(kKBytes + wave * kVG * 1024);
+    load_sub(rkc, kdst, t * row_bytes + chunk * 16, 0);
+    load_sub(rkc, kdst + 1024u, t * row_bytes + chunk * 16, 128);
+    load_sub(rkr, kdst + 2048u, t * kDR * 2 + chunk * 16, 0);
+    load_sub(rv, vdst, t * row_bytes + chunk * 16, 0);
+    load_sub(rv, vdst + 1024u, t * row_bytes + chunk * 16, 128);
   };
+  static_assert(kLoadsPerWave == 5 && kKG == 3 && kVG == 2 && kStep / 8 == kNT / kWave,
+                "one token group of every column group per wave");
 
   // fragment offsets (see the decode kernel: the same layouts with 3 and 2
   // column groups per row instead of 9)

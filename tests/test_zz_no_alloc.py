@@ -43,8 +43,9 @@ def test_noalloc_matches_workspace_decode_two_calls(G):
         compare_sampled(case, u, lse, list(range(case.cfg.batch)))
 
 
-def test_noalloc_fp8_cache():
-    case = DecodeCase(W.scaled(W.CONFIGS["fp8"], batch=6, seq_len=900))
+@pytest.mark.parametrize("name", ["fp8", "fp8p2"])
+def test_noalloc_fp8_cache(name):
+    case = DecodeCase(W.scaled(W.CONFIGS[name], batch=6, seq_len=900))
     u, lse = _noalloc(case, 16)
     ur, lr = case.run(G=16)
     assert torch.equal(u.view(torch.int16), ur.view(torch.int16)) and torch.equal(lse, lr)
