@@ -109,16 +109,16 @@ struct OutProjArgs {
   int act_dtype;
 };
 
-// chunked prefill (un-absorbed form): gather, then expansion by two linear
-// layers, then attention
+// chunked prefill (un-absorbed form): gather and q rotation, the K^C / V
+// expansion, then attention
 struct PrefillArgs {
   const void* q;             // [C][H][d_nope + d_rope] bf16, q^R not yet rotated
   const void* cache;         // paged pool [nblk][bs][D] bf16
   const int32_t* page_table; // the sequence's row
   void* ws_c;                // [T][d_latent] gathered latents
   void* ws_kr;               // [T][d_rope] gathered RoPE keys
-  void* ws_kc;               // [T][H * d_nope] expanded content keys
-  void* ws_v;                // [T][H * d_v] expanded values
+  void* ws_kc;               // [H][T][d_nope] expanded content keys (head-major)
+  void* ws_v;                // [H][T][d_v] expanded values (head-major)
   const void* w_uk;          // [H][d_nope][d_latent] bf16 = [H * d_nope][d_latent]
   const void* w_uv;          // [H][d_v][d_latent] bf16 = [H * d_v][d_latent]
   void* ws_q;                // [C][H][d_nope + d_rope] the queries, q^R rotated

@@ -14,8 +14,8 @@
 //  1. prefill_gather_kernel: the sequence's rows from the paged cache into
 //     contiguous c [T][512] and k^R [T][64]; prefill_rope_kernel: the chunk's
 //     queries with q^R rotated at each token's position;
-//  2. the expansion, two matrix-core linear layers (mla_linear's kernel):
-//     K^C = c W^UK^T [T][H*128] and V = c W^UV^T [T][H*128];
+//  2. prefill_expand_kernel: the expansion K^C = c W^UK^T and V = c W^UV^T,
+//     one persistent GEMM launch for both, written head-major [H][T][128];
 //  3. prefill_attn_kernel: one workgroup per (head, 128 chunk tokens), four
 //     waves of 32 tokens.  Key/value steps of 32 cached tokens (12 KB of keys,
 //     8 KB of values) move HBM -> LDS once with direct loads and serve the
