@@ -315,8 +315,13 @@ int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
  * (the rotation of q^R at the token's position is done here).
  *   q_in           [n_tokens][num_heads][d_nope + d_rope] bf16: per head q^C
  *                  then the not yet rotated q^R (mla_query_absorb's input layout)
- *   cache          the paged pool (bf16); page_table_row [>= ceil(seq_len /
- *                  block_size)] int32: the sequence's row of the page table
+ *   cache          the paged pool: bf16, or e4m3 codes (MLA_FP8_E4M3 or
+ *                  MLA_FP8_E4M3_PO2) with cache_scales [num_blocks][block_size]
+ *                  [5] fp32 as mla_decode reads them (NULL for bf16); e4m3 rows
+ *                  are dequantised (code x tile scale in fp32, one bf16
+ *                  rounding) when the chunk's sequence is gathered
+ *   page_table_row [>= ceil(seq_len / block_size)] int32: the sequence's row
+ *                  of the page table
  *   w_uk           [num_heads][d_nope][d_latent] bf16; w_uv [num_heads][d_v][d_latent]
  *   out            [n_tokens][num_heads][d_v] bf16 (the heads' outputs before W^O)
  *   workspace      mla_prefill_workspace_size(dims, n_tokens, seq_len) bytes,
@@ -324,20 +329,22 @@ int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
  *                  and values ((d_latent + d_rope + 2 * 128 * num_heads) * 2
  *                  bytes per cached token) and the rotated queries
  *                  (n_tokens * num_heads * (d_nope + d_rope) * 2 bytes)
- * Supported: bf16 activations and cache with the DeepSeek-V3 dimensions
- * (H = 128, d_latent = 512, d_rope = 64, d_nope = d_v = 128); other dims
- * return MLA_ERR_UNSUPPORTED (the workspace size is 0).  fp32 accumulation,
+ * Supported: bf16 activations, a bf16 or e4m3 cache, the DeepSeek-V3
+ * dimensions (H = 128, d_latent = 512, d_rope = 64, d_nope = d_v = 128);
+ * other dims or dtypes return MLA_ERR_UNSUPPORTED (the workspace size is 0).  fp32 accumulation,
  * RoPE angles in fp64 with cos/sin rounded to fp32, bf16 outputs.
  * Errors: MLA_ERR_INVALID_ARGUMENT (n_tokens < 0, seq_len < n_tokens, NULL or
- * misaligned pointers: q, cache and weights 16 bytes, out 8),
+ * misaligned pointers: q, cache and weights 16 bytes, out 8; cache_scales
+ * given for a bf16 cache or missing for an e4m3 one),
  * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_UNSUPPORTED.  n_tokens = 0 does
  * nothing.
  */
 size_t mla_prefill_workspace_size(const mla_dims *dims, int32_t n_tokens, int32_t seq_len);
 
 int mla_prefill(const mla_dims *dims, const void *q_in, int32_t n_tokens, const void *cache,
-                const int32_t *page_table_row, int32_t seq_len, const void *w_uk, const void *w_uv,
-                void *out, void *workspace, size_t workspace_bytes, mla_stream_t stream);
+                const float *cache_scales, const int32_t *page_table_row, int32_t seq_len,
+                const void *w_uk, const void *w_uv, void *out, void *workspace, size_t workspace_bytes,
+                mla_stream_t stream);
 
 /*
  * mla_decode_noalloc -- mla_decode followed by mla_decode_combine, for

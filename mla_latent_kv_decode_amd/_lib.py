@@ -99,7 +99,7 @@ def lib():
         L.mla_decode_noalloc.argtypes = [D, _P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _P]
         L.mla_prefill_workspace_size.argtypes = [D, _I, _I]
         L.mla_prefill_workspace_size.restype = ctypes.c_size_t
-        L.mla_prefill.argtypes = [D, _P, _I, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.mla_prefill.argtypes = [D, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]
         for f in ("mla_cache_append", "mla_decode", "mla_decode_combine", "mla_out_proj",
                   "mla_decode_combine_out_proj", "mla_query_absorb", "mla_cache_append_query_absorb",
                   "mla_linear", "mla_decode_noalloc", "mla_prefill"):
@@ -239,9 +239,11 @@ def mla_prefill_workspace_size(dims, n_tokens: int, seq_len: int) -> int:
     return lib().mla_prefill_workspace_size(ctypes.byref(dims), n_tokens, seq_len)
 
 
-def mla_prefill(dims, q_in, cache, page_table_row, seq_len: int, w_uk, w_uv, out, workspace, stream=None):
+def mla_prefill(dims, q_in, cache, page_table_row, seq_len: int, w_uk, w_uv, out, workspace, stream=None,
+                cache_scales=None):
     """q_in [C, H, d_nope + d_rope] (q^R not rotated); page_table_row [max_blocks] int32;
-    out [C, H, d_v]; workspace a uint8 tensor of mla_prefill_workspace_size bytes."""
-    _check(lib().mla_prefill(ctypes.byref(dims), _ptr(q_in), q_in.shape[0], _ptr(cache), _ptr(page_table_row),
-                             seq_len, _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace),
+    out [C, H, d_v]; workspace a uint8 tensor of mla_prefill_workspace_size bytes;
+    cache_scales [nblk, bs, 5] fp32 for an e4m3 cache."""
+    _check(lib().mla_prefill(ctypes.byref(dims), _ptr(q_in), q_in.shape[0], _ptr(cache), _ptr(cache_scales),
+                             _ptr(page_table_row), seq_len, _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream)))

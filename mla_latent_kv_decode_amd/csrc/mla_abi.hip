@@ -619,7 +619,8 @@ PrefillLayout prefill_layout(const mla_dims* d, int n_tokens, int seq_len) {
   return w;
 }
 bool prefill_dims_ok(const mla_dims* d) {
-  return d->act_dtype == MLA_BF16 && d->cache_dtype == MLA_BF16 && d->num_heads == 128 && d->d_latent == 512 &&
+  return d->act_dtype == MLA_BF16 && (d->cache_dtype == MLA_BF16 || mla::is_fp8_cache(d->cache_dtype)) &&
+         d->num_heads == 128 && d->d_latent == 512 &&
          d->d_rope == 64 && d->d_nope == 128 && d->d_v == 128;
 }
 }  // namespace
@@ -630,16 +631,20 @@ size_t mla_prefill_workspace_size(const mla_dims* d, int32_t n_tokens, int32_t s
 }
 
 int mla_prefill(const mla_dims* d, const void* q_in, int32_t n_tokens, const void* cache,
-                const int32_t* page_table_row, int32_t seq_len, const void* w_uk, const void* w_uv, void* out,
-                void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+                const float* cache_scales, const int32_t* page_table_row, int32_t seq_len, const void* w_uk,
+                const void* w_uv, void* out, void* workspace, size_t workspace_bytes, mla_stream_t stream) {
   if (int e = check_dims(d, true)) return e;
   if (n_tokens < 0 || seq_len < n_tokens)
     return fail(MLA_ERR_INVALID_ARGUMENT, "n_tokens=%d seq_len=%d (need 0 <= n_tokens <= seq_len)", n_tokens,
                 seq_len);
   if (n_tokens == 0) return ok();
   if (!prefill_dims_ok(d))
-    return fail(MLA_ERR_UNSUPPORTED, "prefill: bf16 activations and cache with H=128, d_latent=512, d_rope=64, "
-                                     "d_nope=128, d_v=128 only");
+    return fail(MLA_ERR_UNSUPPORTED, "prefill: bf16 activations, a bf16 or e4m3 cache, H=128, d_latent=512, "
+                                     "d_rope=64, d_nope=128, d_v=128 only");
+  if (mla::is_fp8_cache(d->cache_dtype) != (cache_scales != nullptr))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_scales must be given exactly for an e4m3 cache");
+  if (cache_scales && !aligned(cache_scales, 4))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned cache_scales");
   if (!q_in || !cache || !page_table_row || !w_uk || !w_uv || !out || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if (!aligned(q_in, 16) || !aligned(cache, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) || !aligned(out, 8) ||
@@ -652,6 +657,8 @@ int mla_prefill(const mla_dims* d, const void* q_in, int32_t n_tokens, const voi
   mla::PrefillArgs a;
   a.q = q_in;
   a.cache = cache;
+  a.cache_scales = cache_scales;
+  a.cache_dtype = d->cache_dtype;
   a.page_table = page_table_row;
   a.ws_c = ws;
   a.ws_kr = ws + w.kr_off;

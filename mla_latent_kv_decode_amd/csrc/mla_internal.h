@@ -113,7 +113,9 @@ struct OutProjArgs {
 // expansion, then attention
 struct PrefillArgs {
   const void* q;             // [C][H][d_nope + d_rope] bf16, q^R not yet rotated
-  const void* cache;         // paged pool [nblk][bs][D] bf16
+  const void* cache;         // paged pool [nblk][bs][D]: bf16, or e4m3 codes
+  const float* cache_scales; // [nblk][bs][5] fp32 for an e4m3 cache, else NULL
+  int cache_dtype;
   const int32_t* page_table; // the sequence's row
   void* ws_c;                // [T][d_latent] gathered latents
   void* ws_kr;               // [T][d_rope] gathered RoPE keys

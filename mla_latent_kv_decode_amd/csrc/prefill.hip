@@ -149,14 +149,32 @@ __global__ __launch_bounds__(kNT) void prefill_rope_kernel(PrefillArgs a) {
 }
 
 __global__ __launch_bounds__(kNT) void prefill_gather_kernel(PrefillArgs a) {
-  // one 16-byte chunk per thread: row t, chunk k of 72 (64 latent + 8 RoPE)
+  // one 16-byte piece of the bf16 row per thread: row t, piece k of 72 (64
+  // latent + 8 RoPE); an e4m3 row gives each piece from 8 codes x the scale
+  // of their 128-channel tile (fp32 product, one bf16 rounding)
   const int64_t i = int64_t(blockIdx.x) * kNT + threadIdx.x;
   if (i >= int64_t(a.seq_len) * 72) return;
   const int t = int(i / 72), k = int(i % 72);
   const int blk = a.page_table[t / a.block_size];
-  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(a.cache) +
-                                                    (int64_t(blk) * a.block_size + t % a.block_size) * (kDC + kDR) * 2);
-  const uint4 v = src[k];
+  const int64_t row = int64_t(blk) * a.block_size + t % a.block_size;
+  uint4 v;
+  if (a.cache_scales) {
+    const uint2 codes = reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(a.cache) + row * (kDC + kDR))[k];
+    const float sc = a.cache_scales[row * 5 + k / 16];
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t w[2] = {codes.x, codes.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[e]), false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[e]), true);
+      o[2 * e] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+      o[2 * e + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+    }
+    v = uint4{o[0], o[1], o[2], o[3]};
+  } else {
+    v = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(a.cache) + row * (kDC + kDR) * 2)[k];
+  }
   if (k < 64)
     reinterpret_cast<uint4*>(a.ws_c)[int64_t(t) * 64 + k] = v;
   else
@@ -576,6 +594,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_supported(const PrefillArgs& a) {
+  static_assert((kDC + kDR) % 16 == 0 && kDC % 128 == 0, "e4m3 rows: 8-byte pieces, 16 pieces a tile");
   return a.H == kH && a.d_latent == kDC && a.d_rope == kDR && a.d_nope == kDN && a.d_v == kDV &&
          (reinterpret_cast<uintptr_t>(a.q) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.cache) % 16) == 0 &&
          (reinterpret_cast<uintptr_t>(a.out) % 8) == 0;

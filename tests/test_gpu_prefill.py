@@ -7,6 +7,7 @@ expanded keys and values and the probabilities are rounded to bf16 on the GPU.
 Heads are independent, so the larger cases check a sample of heads against
 the oracle run on those heads alone and every output for finiteness.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -36,21 +37,30 @@ class PrefillCase:
     slots and guard blocks hold NaN) and a chunk of C queries and the
     expansion weights, all resident on the GPU."""
 
-    def __init__(self, T: int, C: int, seed: int):
+    def __init__(self, T: int, C: int, seed: int, cache: str = "bf16"):
         d = self.d = V3.dims
         self.T, self.C = T, C
         lens = np.array([T], np.int32)
         table, nblk = W.page_table(lens, d.block_size, seed, shuffle=True, guard_blocks=2)
         self.table = table
         rows = W.cache_rows(nblk * d.block_size, V3, seed=seed + 10, device="cuda")
-        pool = rows.to(torch.bfloat16).view(nblk, d.block_size, d.row)
-        del rows
         used = torch.zeros(nblk, d.block_size, dtype=torch.bool)
         nb = (T + d.block_size - 1) // d.block_size
         flat = torch.zeros(nb * d.block_size, dtype=torch.bool)
         flat[:T] = True
         used[torch.from_numpy(table[0, :nb].astype(np.int64))] = flat.view(nb, d.block_size)
-        pool[(~used).cuda()] = float("nan")
+        self.scales = None
+        if cache == "bf16":
+            pool = rows.to(torch.bfloat16).view(nblk, d.block_size, d.row)
+            pool[(~used).cuda()] = float("nan")
+        else:  # e4m3 codes and tile scales from the oracle's encoder; unused slots NaN codes and scales
+            codes, sc = O.quantize_fp8_rows(rows.cpu().numpy(), pow2_scales=cache == "fp8p2")
+            pool = torch.from_numpy(codes).cuda().view(nblk, d.block_size, d.row)
+            scales = torch.from_numpy(sc).cuda().view(nblk, d.block_size, 5)
+            pool[(~used).cuda()] = 0x7F
+            scales[(~used).cuda()] = float("nan")
+            self.scales = scales
+        del rows
         self.pool = pool
         self.table_t = torch.from_numpy(table[0]).cuda()
         self.q = W.normal((C, d.num_heads, d.d_nope + d.d_rope), seed + 20, device="cuda").to(torch.bfloat16)
@@ -58,14 +68,15 @@ class PrefillCase:
         self.w_uk = W.normal((d.num_heads, d.d_nope, d.d_latent), seed + 30, std=std, device="cuda").to(torch.bfloat16)
         self.w_uv = W.normal((d.num_heads, d.d_v, d.d_latent), seed + 40, std=std, device="cuda").to(torch.bfloat16)
         self.scale = O.softmax_scale(d.d_nope, d.d_rope)
-        self.dims = dims_of(V3)
+        self.dims = dims_of(V3 if cache == "bf16" else dataclasses.replace(V3, cache_dtype=cache))
 
     def run(self):
         import mla_latent_kv_decode_amd as M
         d = self.d
         ws = torch.empty(M.mla_prefill_workspace_size(self.dims, self.C, self.T), dtype=torch.uint8, device="cuda")
         out = torch.empty(self.C, d.num_heads, d.d_v, dtype=torch.bfloat16, device="cuda")
-        M.mla_prefill(self.dims, self.q, self.pool, self.table_t, self.T, self.w_uk, self.w_uv, out, ws)
+        M.mla_prefill(self.dims, self.q, self.pool, self.table_t, self.T, self.w_uk, self.w_uv, out, ws,
+                      cache_scales=self.scales)
         torch.cuda.synchronize()
         return out
 
@@ -73,7 +84,11 @@ class PrefillCase:
         d = self.d
         nb = (self.T + d.block_size - 1) // d.block_size
         idx = torch.from_numpy(self.table[0, :nb].astype(np.int64)).cuda()
-        return to_f64(self.pool.index_select(0, idx)).reshape(nb * d.block_size, d.row)[:self.T]
+        if self.scales is None:
+            return to_f64(self.pool.index_select(0, idx)).reshape(nb * d.block_size, d.row)[:self.T]
+        codes = self.pool.index_select(0, idx).cpu().numpy().reshape(nb * d.block_size, d.row)[:self.T]
+        sc = self.scales.index_select(0, idx).cpu().numpy().reshape(nb * d.block_size, 5)[:self.T]
+        return O.dequantize_fp8_rows(codes, sc)
 
     def oracle(self, heads) -> np.ndarray:
         d = self.d
@@ -124,6 +139,21 @@ def test_prefill_full_size_chunk(T, C, seed):
     assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2, (T, C)
 
 
+@pytest.mark.parametrize("cache", ["fp8", "fp8p2"])
+@pytest.mark.parametrize("T,C", [(300, 77), (1000, 257)])
+def test_prefill_over_fp8_cache(cache, T, C):
+    """An e4m3 cache (tile scales of any value, or powers of two): the gather
+    dequantises each value (code x scale, one bf16 rounding, exact for
+    powers of two) and the rest is the bf16 path; against the oracle on the
+    dequantised rows, with the bf16 bars."""
+    case = PrefillCase(T, C, seed=600 + T + C, cache=cache)
+    out = case.run()
+    assert torch.isfinite(out).all()
+    ref = case.oracle(SAMPLE_HEADS)
+    got = to_f64(out)[:, SAMPLE_HEADS]
+    assert rel_l2(got, ref) <= 1e-2 and max_abs(got, ref) <= 2e-2, (cache, T, C)
+
+
 def test_prefill_matches_absorbed_decode_on_gpu():
     """The same chunk through the absorbed decode path (q absorbed and rotated
     at positions T - C + j, decode with n_q = C, combine, W^UV projection)
@@ -161,3 +191,10 @@ def test_prefill_rejects_bad_arguments():
     with pytest.raises(RuntimeError):
         M.mla_prefill(case.dims, case.q, case.pool, case.table_t, case.C - 1, case.w_uk, case.w_uv, out, ws)
     assert M.mla_prefill_workspace_size(case.dims, 9, 8) == 0
+    # scales exactly for an e4m3 cache
+    with pytest.raises(RuntimeError, match="cache_scales"):
+        M.mla_prefill(case.dims, case.q, case.pool, case.table_t, case.T, case.w_uk, case.w_uv, out, ws,
+                      cache_scales=torch.ones(4, dtype=torch.float32, device="cuda"))
+    f8 = PrefillCase(64, 8, seed=4, cache="fp8")
+    with pytest.raises(RuntimeError, match="cache_scales"):
+        M.mla_prefill(f8.dims, f8.q, f8.pool, f8.table_t, f8.T, f8.w_uk, f8.w_uv, out, ws)
