@@ -333,6 +333,9 @@ int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
  * dimensions (H = 128, d_latent = 512, d_rope = 64, d_nope = d_v = 128);
  * other dims or dtypes return MLA_ERR_UNSUPPORTED (the workspace size is 0).  fp32 accumulation,
  * RoPE angles in fp64 with cos/sin rounded to fp32, bf16 outputs.
+ * The page-table entries the chunk's sequence needs (ceil(seq_len /
+ * block_size) of them) must lie in the pool; they are not checked, and
+ * validation mode does not cover this call.
  * Errors: MLA_ERR_INVALID_ARGUMENT (n_tokens < 0, seq_len < n_tokens, NULL or
  * misaligned pointers: q, cache and weights 16 bytes, out 8; cache_scales
  * given for a bf16 cache or missing for an e4m3 one),
