@@ -288,14 +288,23 @@ MLA_DEV void convert_step_f8(unsigned char* dst, const unsigned char* stage, int
   typedef __attribute__((address_space(3))) u32x4 lds_u4w;
   typedef __attribute__((address_space(3))) const float lds_f32;
   typedef float f32x2 __attribute__((ext_vector_type(2)));
+  constexpr int kUnits = kStep * (kD / 16);  // 1152 units of 16 codes: token u / 36, chunk u % 36
+  static_assert(kUnits > 4 * kNT && kUnits <= 5 * kNT && (kUnits - 4 * kNT) % kWave == 0 && kNT == 7 * 36 + 4,
+                "units tid + 256 i: four for every thread, a fifth for whole waves; 256 = 7 x 36 + 4");
   const uint32_t sb = lds_addr(stage), db = lds_addr(dst);
-#pragma unroll 1
-  for (int u = tid_fresh(); u < kStep * (kD / 16); u += kNT) {
-    const int t = u / (kD / 16), c8 = u % (kD / 16);
-    const u32x4 cw = *(lds_u4*)(uintptr_t)(sb + t * kD + c8 * 16);
-    const float sc_raw = *(lds_f32*)(uintptr_t)(sb + kF8Codes + (t * 5 + c8 / 8) * 4);
+  const int tid = tid_fresh();
+  const int t0 = tid / 36, c0 = tid % 36;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    if (i == 4 && tid >= kUnits - 4 * kNT) break;  // (wave-uniform)
+    // unit u = tid + 256 i: its codes are the contiguous 16 bytes at u * 16
+    // of the staged step; its token and chunk follow from (t0, c0)
+    const int cw = c0 + 4 * i, carry = cw >= 36;
+    const int c8 = cw - 36 * carry, t = t0 + 7 * i + carry;
+    const u32x4 cwv = *(lds_u4*)(uintptr_t)(sb + uint32_t(tid * 16 + i * kNT * 16));
+    const float sc_raw = *(lds_f32*)(uintptr_t)(sb + uint32_t(kF8Codes + (t * 5 + c8 / 8) * 4));
     const float sc = t < nvalid ? sc_raw : 0.f;
-    const uint32_t w[4] = {cw[0], cw[1], cw[2], cw[3]};
+    const uint32_t w[4] = {cwv[0], cwv[1], cwv[2], cwv[3]};
     uint32_t o[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -304,8 +313,11 @@ MLA_DEV void convert_step_f8(unsigned char* dst, const unsigned char* stage, int
       o[2 * e] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
       o[2 * e + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
     }
-    *(lds_u4w*)(uintptr_t)(db + step_off(t, 2 * c8)) = u32x4{o[0], o[1], o[2], o[3]};
-    *(lds_u4w*)(uintptr_t)(db + step_off(t, 2 * c8 + 1)) = u32x4{o[4], o[5], o[6], o[7]};
+    // bf16 chunks 2 c8 and 2 c8 + 1 of token t: the same 128-byte row, slots
+    // differing in their lowest bit
+    const uint32_t d0 = db + uint32_t(step_off(t, 2 * c8));
+    *(lds_u4w*)(uintptr_t)d0 = u32x4{o[0], o[1], o[2], o[3]};
+    *(lds_u4w*)(uintptr_t)(d0 ^ 16u) = u32x4{o[4], o[5], o[6], o[7]};
   }
 }
 
