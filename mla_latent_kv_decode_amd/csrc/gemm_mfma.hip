@@ -164,8 +164,16 @@ __global__ __launch_bounds__(kNT) void append_partial_tiled_kernel(AppendArgs a,
   extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
   AppTileSmem& sm = *reinterpret_cast<AppTileSmem*>(smem_raw);
   const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int c0 = blockIdx.x * kTC, kc = blockIdx.y, t0 = blockIdx.z * kTT;
   const int T = a.n_tokens, D = a.D, dm = a.d_model, dc = a.d_latent;
+  // Slice-major and XCD-aware: workgroups are dealt round-robin to the 8
+  // XCDs, so consecutive logical ids share one, and all column and token
+  // tiles of a k slice (which share its h and W tiles) land on the same
+  // XCD and read those tiles from HBM once between them.
+  const int nct = D / kTC, ntt = (T + kTT - 1) / kTT;
+  const int NB = gridDim.x, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;
+  const int kc = logical / (nct * ntt), rem = logical % (nct * ntt);
+  const int t0 = (rem / nct) * kTT, c0 = (rem % nct) * kTC;
   const int64_t k0 = int64_t(kc) * kTK;
   const unsigned char* hsrc = static_cast<const unsigned char*>(a.h) + (int64_t(t0) * dm + k0) * 2;
   const unsigned char* wsrc =
@@ -257,7 +265,7 @@ hipError_t launch_append_partial_mfma(const AppendArgs& a, void* ws, hipStream_t
                                           int(sizeof(AppTileSmem)));
         e != hipSuccess)
       return e;
-    dim3 g1(unsigned(a.D / kTC), unsigned(nk), unsigned((a.n_tokens + kTT - 1) / kTT));
+    const dim3 g1(unsigned(a.D / kTC) * unsigned(nk) * unsigned((a.n_tokens + kTT - 1) / kTT));
     hipLaunchKernelGGL(append_partial_tiled_kernel, g1, dim3(kNT), sizeof(AppTileSmem), st, a,
                        static_cast<float*>(ws));
   } else {

@@ -7,10 +7,11 @@
 // written packed as [q~_i ; q^R_i], the layout the decode kernels read.
 //
 // Matrix-core form (bf16, d_latent = 512, d_nope = 128):
-// one workgroup per (head, quarter of the 512 columns), all rows.
+// one workgroup per (head, quarter of the 512 columns, split of the rows:
+// up to four groups of 32 rows each).
 //  * The W^UK_i quarter (d_nope rows of 256 bytes) is copied into LDS by
 //    direct 1 KB loads, the 16-byte chunks of row n XOR-swizzled by
-//    (n & 3) << 2; every W byte is read once per call.
+//    (n & 3) << 2; every W byte is read once per row split.
 //  * The product is out[rows][c] = q^C[rows][n] . W^UK_i[n][c]: the
 //    A operand (q^C, 16 contiguous bytes along n per lane) comes straight
 //    from global memory; the B operand needs 8 consecutive n of one column
@@ -65,7 +66,17 @@ MLA_DEV void rope_pair(float x, float z, int pos, double inv_freq, float* y0, fl
 }
 MLA_DEV double rope_inv_freq(int j, int half, float base) { return pow(double(base), -double(j) / double(half)); }
 
-// Block blk of NB (NB = 4 H); blk % 8 is the XCD the block runs on.
+// Row splits: each workgroup takes up to kGroupsPerSplit groups of 32 rows
+// (a longer serial walk over the row groups leaves the compute unit waiting
+// on each group's loads); the W quarter is then read once per split, the
+// later ones from L2.
+constexpr int kGroupsPerSplit = 4;
+MLA_HD inline int absorb_row_splits(int rows) {
+  const int groups = (rows + kRows - 1) / kRows;
+  return max(1, (groups + kGroupsPerSplit - 1) / kGroupsPerSplit);
+}
+
+// Block blk of NB (NB = 4 H x row splits); blk % 8 is the XCD the block runs on.
 MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
   __shared__ __attribute__((aligned(128))) unsigned char w_lds[kMaxNope * kQRow];    // W^UK_i quarter
   __shared__ __attribute__((aligned(128))) unsigned char o_lds[kRows * kQRow];       // output stage
@@ -74,18 +85,25 @@ MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int H = a.H, dn = a.d_nope, dr = a.d_rope, R = a.rows;
   const int in_stride = dn + dr, out_stride = kDL + dr;
-  // the four column quarters of one head run on one XCD and share its L2 for q^C
+  // the column quarters and row splits of one head run on one XCD and share
+  // its L2 for q^C (per split) and the W quarters (per quarter)
   const int xcd = blk % 8, idx = blk / 8;
   const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;
-  const int h = __builtin_amdgcn_readfirstlane(logical / kQuarters);
+  const int RS = absorb_row_splits(R);
+  const int h = __builtin_amdgcn_readfirstlane(logical / (kQuarters * RS));
+  const int rs = __builtin_amdgcn_readfirstlane((logical / kQuarters) % RS);
   const int cq = __builtin_amdgcn_readfirstlane(logical % kQuarters);
+  // this workgroup's rows [r_lo, r_hi): whole groups of 32
+  const int rows_per = ((R + kRows - 1) / kRows + RS - 1) / RS * kRows;
+  const int r_lo = rs * rows_per, r_hi = min(R, r_lo + rows_per);
+  if (r_lo >= R) return;  // (workgroup-uniform: no barrier is left waiting)
 
   // ---- RoPE inputs of this workgroup's first 32 rows r = cq (mod 4), loaded
   //      before anything else: loads complete in order, so behind the W tile
   //      they would wait for all of it (unconditional loads of clamped
   //      indices; the unused ones are never stored) ----
   const int half = dr / 2;
-  const int rope_rows = (R - cq + kQuarters - 1) / kQuarters;
+  const int rope_rows = max(0, (r_hi - r_lo - cq + kQuarters - 1) / kQuarters);  // rows r_lo + cq + 4k
   const __bf16* qin = static_cast<const __bf16*>(a.q_in);
   float rx[kRopePerThread], rz[kRopePerThread];
   int rpos[kRopePerThread];
@@ -93,7 +111,7 @@ MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
   for (int k = 0; k < kRopePerThread; ++k) {
     const int it = tid + kNT * k, hh = max(half, 1);
     const int kk = min(it / hh, max(rope_rows - 1, 0)), j = it % hh;
-    const int rr = min(cq + kQuarters * kk, R - 1);
+    const int rr = min(r_lo + cq + kQuarters * kk, R - 1);
     const size_t ib = (size_t(rr) * H + h) * in_stride + dn;
     rx[k] = float(qin[ib + min(j, max(dr - 1, 0))]);
     rz[k] = float(qin[ib + min(j + half, max(dr - 1, 0))]);
@@ -109,7 +127,7 @@ MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
     for (int s = 0; s < kMaxNope / 16; ++s) af[s] = *reinterpret_cast<const bf16x8*>(arow + 16 * s);
   };
   bf16x8 af_cur[kMaxNope / 16], af_nxt[kMaxNope / 16];
-  load_a(0, af_cur);
+  load_a(r_lo, af_cur);
 
   // ---- W^UK_i[:, 128 cq .. 128 cq + 127] -> LDS: rows of 256 bytes, four
   //      rows per direct 1 KB load, chunks of row n swizzled by (n & 3) << 2 ----
@@ -157,7 +175,7 @@ MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
       for (int i = tid; i < kRows * cpr; i += kNT) {
         const int k = rb + i / cpr, c = i % cpr;
         if (k < rope_rows) {
-          const int rr = cq + kQuarters * k;
+          const int rr = r_lo + cq + kQuarters * k;
           *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(qout) +
                                     ((size_t(rr) * H + h) * out_stride + kDL) * 2 + c * 16) =
               *reinterpret_cast<const uint4*>(r_lds + (i / cpr) * dr * 2 + c * 16);
@@ -165,20 +183,9 @@ MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
       }
       lds_barrier();
     };
+    // a split's rows r = cq (mod 4) fit one block of 32
+    static_assert(kGroupsPerSplit * kRows / kQuarters <= kRows, "one RoPE block per workgroup");
     if (rope_rows > 0) emit(0, rx, rz, rpos);
-    for (int rb = kRows; rb < rope_rows; rb += kRows) {  // more than 128 rows: later blocks
-#pragma unroll
-      for (int k = 0; k < kRopePerThread; ++k) {
-        const int it = tid + kNT * k, hh = max(half, 1);
-        const int kk = min(rb + it / hh, rope_rows - 1), j = it % hh;
-        const int rr = cq + kQuarters * kk;
-        const size_t ib = (size_t(rr) * H + h) * in_stride + dn;
-        rx[k] = float(qin[ib + min(j, dr - 1)]);
-        rz[k] = float(qin[ib + min(j + half, dr - 1)]);
-        rpos[k] = a.positions[rr];
-      }
-      emit(rb, rx, rz, rpos);
-    }
   }
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -205,9 +212,9 @@ MLA_DEV void query_absorb_mfma_body(const QueryArgs& a, int blk, int NB) {
 
   // ---- row groups of 32: A from global, 8 MFMAs, staged, written in
   //      256-byte row segments ----
-  for (int r0 = 0; r0 < R; r0 += kRows) {
-    const int nrows = min(kRows, R - r0);
-    if (r0 + kRows < R) load_a(r0 + kRows, af_nxt);  // the next group's A, in flight meanwhile
+  for (int r0 = r_lo; r0 < r_hi; r0 += kRows) {
+    const int nrows = min(kRows, r_hi - r0);
+    if (r0 + kRows < r_hi) load_a(r0 + kRows, af_nxt);  // the next group's A, in flight meanwhile
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < kMaxNope / 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_cur[s], bf[s], acc, 0, 0, 0);
@@ -292,13 +299,14 @@ bool query_absorb_mfma_supported(const QueryArgs& a) {
 }
 
 hipError_t launch_query_absorb_mfma(const QueryArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(query_absorb_mfma_kernel, dim3(unsigned(a.H) * kQuarters), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL(query_absorb_mfma_kernel, dim3(unsigned(a.H) * kQuarters * unsigned(absorb_row_splits(a.rows))),
+                     dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_append_finalize_query_mfma(const AppendArgs& ap, const void* ws, const QueryArgs& q,
                                              hipStream_t st) {
-  const int nk = append_mfma_slices(ap), nq = q.H * kQuarters;
+  const int nk = append_mfma_slices(ap), nq = q.H * kQuarters * absorb_row_splits(q.rows);
   const dim3 grid(unsigned(nq + (append_finalize_units(ap) + 1) / 2));
   const float* w = static_cast<const float*>(ws);
   if (ap.cache_dtype == MLA_BF16)

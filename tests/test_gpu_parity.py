@@ -220,7 +220,7 @@ def _query_case(H, d_nope, d_rope, d_latent, rows, seed, dtype):
     return q_in, w_uk, torch.from_numpy(pos).cuda(), ref
 
 
-@pytest.mark.parametrize("rows", [1, 64, 70, 300])  # 300: RoPE rows in three blocks per workgroup
+@pytest.mark.parametrize("rows", [1, 64, 70, 300, 512])  # 300: three row splits, the last ragged
 def test_query_absorb_v3_bf16(rows):
     import mla_latent_kv_decode_amd as M
     d = W.V3
