@@ -59,7 +59,7 @@ MLA_DEV float e4m3_to_f32(uint32_t c) {
 
 // fp32 -> E4M3, round to nearest even, magnitudes >= 448 saturate to 448.
 // Either e4m3 cache format (tile scales of any value, or powers of two).
-MLA_HD inline bool is_fp8_cache(int dt) { return dt == MLA_FP8_E4M3 || dt == MLA_FP8_E4M3_PO2; }
+MLA_HD bool is_fp8_cache(int dt) { return dt == MLA_FP8_E4M3 || dt == MLA_FP8_E4M3_PO2; }
 
 // Exponent E of a power-of-two tile scale: the smallest integer with
 // amax <= 448 * 2^E (amax > 0 and finite).  With amax = 1.m * 2^e and

@@ -71,7 +71,7 @@ MLA_DEV double rope_inv_freq(int j, int half, float base) { return pow(double(ba
 // on each group's loads); the W quarter is then read once per split, the
 // later ones from L2.
 constexpr int kGroupsPerSplit = 4;
-MLA_HD inline int absorb_row_splits(int rows) {
+MLA_HD int absorb_row_splits(int rows) {
   const int groups = (rows + kRows - 1) / kRows;
   return max(1, (groups + kGroupsPerSplit - 1) / kGroupsPerSplit);
 }

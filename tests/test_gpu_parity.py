@@ -868,6 +868,9 @@ FUSED = [
     (W.scaled(W.CONFIGS["v3"], batch=128, seq_len=200), 0),                 # 128 rows: 2 groups each
     (W.scaled(W.CONFIGS["ragged"], batch=256, len_lo=2, len_hi=600), 0),   # 512 rows, n_q = 2: 8 groups
     (W.scaled(W.CONFIGS["v3"], batch=200, seq_len=130), 0),                 # 7 groups, 3 per workgroup: last has 1
+    # several groups per workgroup and several 4-piece chunks per row
+    (W.scaled(W.CONFIGS["v3"], batch=128, seq_len=1500), 1024),             # about 8 pieces a row
+    (W.scaled(W.CONFIGS["ragged"], batch=256, len_lo=2, len_hi=700), 1024),  # 512 rows, 1 to ~10 pieces
 ]
 ROW_MODE_MAX_ROWS = 32  # the fused kernel gives each (head, row) its own workgroup up to here
 
