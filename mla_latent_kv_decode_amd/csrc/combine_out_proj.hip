@@ -149,7 +149,6 @@ void combine_out_proj_kernel(CombineProjArgs a, int gpw) {
       l_lrow = lrow[i];
     }
   for (int s0 = 0; s0 < maxnp; s0 += kPC) {
-    float ls[kRowsPerWave][kPC];
     uint4 x[kRowsPerWave][kPC];
     // Loads are unconditional (a branch around each would make the wave wait
     // for every load before issuing the next): a piece past the row's count
@@ -166,29 +165,32 @@ void combine_out_proj_kernel(CombineProjArgs a, int gpw) {
         x[i][s] = *reinterpret_cast<const uint4*>(orow_ws[i] + (np[i] > 0 ? off * kDC : 0));
       }
     __builtin_amdgcn_sched_barrier(0);  // every load of the chunk is issued before the first use
+    // The chunk's weights are computed one (row, piece) per lane, lane l < 32
+    // holding row l / kPC and piece s0 + l % kPC: the same expf of the same
+    // operands as a per-row loop would take (so the merge stays bit-identical
+    // to mla_decode_combine's), two per lane instead of forty wave-uniform
+    // ones, then read back per row.
+    const float ls_l = s0 + lsp < ln_np ? lse_l : -INFINITY;  // mask pieces past the row's count
+    float mc_l = fmaxf(ls_l, __shfl_xor(ls_l, 1, kWave));     // the row's four lanes
+    mc_l = fmaxf(mc_l, __shfl_xor(mc_l, 2, kWave));
+    float m_l = M[0];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i)
-#pragma unroll
-      for (int s = 0; s < kPC; ++s) ls[i][s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse_l), i * kPC + s));
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i)
-#pragma unroll
-      for (int s = 0; s < kPC; ++s)
-        if (s0 + s >= np[i]) ls[i][s] = -INFINITY;  // mask pieces past the row's count
+    for (int i = 1; i < kRowsPerWave; ++i)
+      if (li == i) m_l = M[i];
+    const float mn_l = fmaxf(m_l, mc_l);
+    const float sc_l = m_l == -INFINITY ? 0.f : expf(m_l - mn_l);  // rescale earlier chunks
+    const float w_l = ls_l == -INFINITY ? 0.f : expf(ls_l - mn_l);
+    auto lane_f = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-      float mc = ls[i][0];
-#pragma unroll
-      for (int s = 1; s < kPC; ++s) mc = fmaxf(mc, ls[i][s]);
-      const float Mn = fmaxf(M[i], mc);
-      const float sc = M[i] == -INFINITY ? 0.f : expf(M[i] - Mn);  // rescale earlier chunks
-      M[i] = Mn;
+      const float sc = lane_f(sc_l, i * kPC);
+      M[i] = lane_f(mn_l, i * kPC);
       wsum[i] *= sc;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[i][e] *= sc;
 #pragma unroll
       for (int s = 0; s < kPC; ++s) {
-        const float w = ls[i][s] == -INFINITY ? 0.f : expf(ls[i][s] - Mn);
+        const float w = lane_f(w_l, i * kPC + s);
         wsum[i] += w;
         if (w != 0.f) {
           const uint32_t v[4] = {x[i][s].x, x[i][s].y, x[i][s].z, x[i][s].w};
