@@ -336,12 +336,13 @@ int mla_decode_combine_out_proj(const mla_dims *dims, const void *workspace,
  * The page-table entries the chunk's sequence needs (ceil(seq_len /
  * block_size) of them) must lie in the pool; they are not checked, and
  * validation mode does not cover this call.
- * Errors: MLA_ERR_INVALID_ARGUMENT (n_tokens < 0, seq_len < n_tokens, NULL or
- * misaligned pointers: q, cache and weights 16 bytes, out 8; cache_scales
- * given for a bf16 cache or missing for an e4m3 one),
- * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_UNSUPPORTED.  n_tokens = 0 does
- * nothing.
+ * Errors: MLA_ERR_INVALID_ARGUMENT (n_tokens < 0, seq_len < n_tokens,
+ * seq_len >= MLA_MAX_PREFILL_TOKENS, NULL or misaligned pointers: q, cache
+ * and weights 16 bytes, out 8; cache_scales given for a bf16 cache or missing
+ * for an e4m3 one), MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_UNSUPPORTED.
+ * n_tokens = 0 does nothing.
  */
+#define MLA_MAX_PREFILL_TOKENS (1 << 23) /* a head's expanded keys stay under 2 GiB */
 size_t mla_prefill_workspace_size(const mla_dims *dims, int32_t n_tokens, int32_t seq_len);
 
 int mla_prefill(const mla_dims *dims, const void *q_in, int32_t n_tokens, const void *cache,

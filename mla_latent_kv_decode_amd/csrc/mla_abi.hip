@@ -641,6 +641,9 @@ int mla_prefill(const mla_dims* d, const void* q_in, int32_t n_tokens, const voi
   if (!prefill_dims_ok(d))
     return fail(MLA_ERR_UNSUPPORTED, "prefill: bf16 activations, a bf16 or e4m3 cache, H=128, d_latent=512, "
                                      "d_rope=64, d_nope=128, d_v=128 only");
+  if (seq_len >= MLA_MAX_PREFILL_TOKENS)  // one head's expanded keys must stay under 2 GiB (32-bit offsets)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "seq_len=%d (prefill takes fewer than %d cached tokens)", seq_len,
+                MLA_MAX_PREFILL_TOKENS);
   if (mla::is_fp8_cache(d->cache_dtype) != (cache_scales != nullptr))
     return fail(MLA_ERR_INVALID_ARGUMENT, "cache_scales must be given exactly for an e4m3 cache");
   if (cache_scales && !aligned(cache_scales, 4))

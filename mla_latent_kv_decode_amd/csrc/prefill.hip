@@ -408,28 +408,32 @@ __global__ __launch_bounds__(kNT, 2) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int row_bytes = kDN * 2;
   const unsigned char* kc_head = static_cast<const unsigned char*>(a.ws_kc) + int64_t(h) * T * row_bytes;
   const unsigned char* v_head = static_cast<const unsigned char*>(a.ws_v) + int64_t(h) * T * row_bytes;
+  // One descriptor per operand for the whole key range: a step's rows are
+  // addressed by soffset (step start) + voffset (this lane's row and chunk),
+  // and the range check counts both, so rows past T still read as zeros.
+  // Built once, outside the step loop (per step they cost about 20 scalar
+  // instructions in a loop bound by instruction issue).
+  const __amdgpu_buffer_rsrc_t rkc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kc_head, (short)0, T * row_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)v_head, (short)0, T * row_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rkr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.ws_kr, (short)0, T * kDR * 2, 0x00020000);
   auto issue_step = [&](int s) __attribute__((always_inline)) {
     const int t0 = s * kStep;
-    const int nvalid = min(kStep, T - t0);
     unsigned char* buf = smem + (s % kNBuf) * kBufBytes;
-    const unsigned char* kc = kc_head + int64_t(t0) * row_bytes;
-    const unsigned char* vv = v_head + int64_t(t0) * row_bytes;
-    const unsigned char* kr = static_cast<const unsigned char*>(a.ws_kr) + int64_t(t0) * kDR * 2;
-    // descriptors cover the live rows only: rows past T read as zeros
-    const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, nvalid * row_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vv, (short)0, nvalid * row_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rkr = __builtin_amdgcn_make_buffer_rsrc((void*)kr, (short)0, nvalid * kDR * 2, 0x00020000);
     // wave w loads token group w (8 tokens) of every column group: K^C
     // twice, k^R, V twice -- the same five loads in every wave, no branches
     const int t = wave * 8 + lane / 8;  // token inside the step
     const int chunk = (lane % 8) ^ swz(t);
     const uint32_t kdst = lds_addr(buf) + uint32_t(wave * kKG * 1024);
     const uint32_t vdst = lds_addr(buf) + uint32_t(kKBytes + wave * kVG * 1024);
-    load_sub(rkc, kdst, t * row_bytes + chunk * 16, 0);
-    load_sub(rkc, kdst + 1024u, t * row_bytes + chunk * 16, 128);
-    load_sub(rkr, kdst + 2048u, t * kDR * 2 + chunk * 16, 0);
-    load_sub(rv, vdst, t * row_bytes + chunk * 16, 0);
-    load_sub(rv, vdst + 1024u, t * row_bytes + chunk * 16, 128);
+    const int so = t0 * row_bytes, sor = t0 * kDR * 2;
+    load_sub(rkc, kdst, t * row_bytes + chunk * 16, so);
+    load_sub(rkc, kdst + 1024u, t * row_bytes + chunk * 16, so + 128);
+    load_sub(rkr, kdst + 2048u, t * kDR * 2 + chunk * 16, sor);
+    load_sub(rv, vdst, t * row_bytes + chunk * 16, so);
+    load_sub(rv, vdst + 1024u, t * row_bytes + chunk * 16, so + 128);
   };
   static_assert(kLoadsPerWave == 5 && kKG == 3 && kVG == 2 && kStep / 8 == kNT / kWave,
                 "one token group of every column group per wave");

@@ -203,3 +203,24 @@ def test_linear_validates_and_sizes_its_workspace(L):
     assert "overlap" in lib.mla_last_error().decode()
     assert call(ctypes.byref(d), wsb=ws - 1) == L.ERR_WORKSPACE_TOO_SMALL
     assert call(ctypes.byref(d), wsp=None) == L.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_prefill_validates(L):
+    """mla_prefill rejects bad lengths and pointers before launching anything,
+    including a cached length whose expanded keys would pass 2 GiB per head."""
+    lib = L.lib()
+    d = _dims(L)
+    call = lambda dims, n=4, seq=100, q=FAKE, sc=None, ws_bytes=1 << 40: lib.mla_prefill(
+        dims, q, n, FAKE, sc, FAKE, seq, FAKE, FAKE, FAKE * 2, FAKE, ws_bytes, None)
+    assert call(None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), n=-1) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), n=5, seq=4) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), n=0, seq=4) == L.OK       # nothing to do
+    assert call(ctypes.byref(d), q=None) == L.ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(d), sc=FAKE) == L.ERR_INVALID_ARGUMENT  # scales for a bf16 cache
+    limit = 1 << 23
+    assert call(ctypes.byref(d), seq=limit) == L.ERR_INVALID_ARGUMENT
+    assert "seq_len" in lib.mla_last_error().decode()
+    assert call(ctypes.byref(d), ws_bytes=16) == L.ERR_WORKSPACE_TOO_SMALL
+    odd = _dims(L, num_heads=64)
+    assert call(ctypes.byref(odd)) == L.ERR_UNSUPPORTED
