@@ -260,54 +260,66 @@ void combine_out_proj_kernel(CombineProjArgs a, int gpw) {
 
 // ---------------------------------------------------------------------------
 // Few rows (R <= 32, e.g. a handful of long sequences): one workgroup per
-// (head, row).  The four waves split the row's pieces (wave w merges pieces
-// w, w + 4, ...), meet in LDS, and the 256 threads then form the d_v outputs
-// as dot products against W^UV_i in LDS (two threads per output, 256 channels
-// each).  With 64 pieces a row this spreads the merge over H x R workgroups
-// of four busy waves instead of H workgroups with one.
+// (head, RPW rows), RPW = 1 or 2.  The 4 / RPW waves of a row split its
+// pieces (wave w of the row merges pieces w, w + 4 / RPW, ...), meet in LDS,
+// and the 256 threads then form the d_v outputs of each row as dot products
+// against W^UV_i in LDS (two threads per output, 256 channels each).  With 64
+// pieces a row this spreads the merge over many workgroups of busy waves
+// instead of H workgroups with one; two rows per workgroup (when that still
+// leaves about one workgroup per compute unit) read each head's W^UV_i half
+// as often.
 // ---------------------------------------------------------------------------
 constexpr int kMaxRowModeRows = 32;
+constexpr int kMaxRPW = 2;
 struct RowSmem {
   alignas(128) unsigned char w[kMaxDV * kRowBytes];  // W^UV_i, rows swizzled as above
   alignas(16) float acc[kNT / kWave][kDC];           // per-wave unnormalised sums
-  alignas(16) unsigned char u[kRowBytes];            // merged row (bf16)
+  alignas(16) unsigned char u[kMaxRPW][kRowBytes];   // merged rows (bf16)
   float mw[kNT / kWave], sw[kNT / kWave];
 };
 
+template <int kRPW>
 __global__ __launch_bounds__(kNT, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void combine_out_proj_row_kernel(CombineProjArgs a) {
+  constexpr int kWPR = (kNT / kWave) / kRPW;  // waves per row
+  static_assert(kRPW >= 1 && kRPW <= kMaxRPW && kWPR * kRPW == kNT / kWave, "rows per workgroup");
   extern __shared__ __attribute__((aligned(128))) unsigned char smem_raw[];
   RowSmem& sm = *reinterpret_cast<RowSmem*>(smem_raw);
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int R = a.batch * a.n_q, H = a.H, dv = a.d_v;
+  const int nrb = (R + kRPW - 1) / kRPW;  // row blocks per head
   const int NB = gridDim.x, xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
   const int logical = xcd * (NB / 8) + min(xcd, NB % 8) + idx;  // rows of one head share an XCD
-  const int h = logical / R, r = logical % R;
+  const int h = logical / nrb, r0 = (logical % nrb) * kRPW;
+  const int nr = min(kRPW, R - r0);  // rows of this workgroup
+  // this wave's row and its place among the row's waves
+  const int q = wave / kWPR, wr = wave % kWPR;
+  const int r = r0 + min(q, nr - 1);
   const int b = r / a.n_q, j = r % a.n_q;
 
   // ---- 0. the row's first slot and piece count (as the decode recorded
   // them), then W^UV_i into LDS ----
   const int slot0 = __builtin_amdgcn_readfirstlane(a.ws_tab[2 * b]);
-  const int np = __builtin_amdgcn_readfirstlane(a.ws_tab[2 * b + 1]);
+  const int np = q < nr ? __builtin_amdgcn_readfirstlane(a.ws_tab[2 * b + 1]) : 0;
   asm volatile("" ::"s"(slot0), "s"(np));  // waited for before the W loads are issued
   load_w_rows(sm.w, a.w_uv, h, dv, wave, lane);
 
-  // ---- 2. this wave's pieces: w, w + 4, ... (lane = 8 channels) ----
+  // ---- 2. this wave's pieces: wr, wr + kWPR, ... (lane = 8 channels) ----
   const size_t pstride = size_t(a.n_q) * H;
   const size_t rbase = (size_t(slot0) * a.n_q + j) * H + h;
   const float* lrow = a.ws_lse + rbase;
   const uint16_t* orow = static_cast<const uint16_t*>(a.ws_o) + rbase * kDC + 8 * lane;
-  const int npw = np > wave ? (np - wave + 3) / 4 : 0;
+  const int npw = np > wr ? (np - wr + kWPR - 1) / kWPR : 0;
   float Mw = -INFINITY, swv = 0.f, acc[8] = {};
   for (int k0 = 0; k0 < npw; k0 += kPC) {
     // unconditional loads of clamped pieces, masked after (see the row-group kernel)
-    const int pl = wave + 4 * min(k0 + lane % kPC, npw - 1);
+    const int pl = wr + kWPR * min(k0 + lane % kPC, npw - 1);
     const float lse_l = lrow[size_t(pl) * pstride];
     uint4 x[kPC];
 #pragma unroll
     for (int s = 0; s < kPC; ++s) {
-      const int p = wave + 4 * min(k0 + s, npw - 1);
+      const int p = wr + kWPR * min(k0 + s, npw - 1);
       x[s] = *reinterpret_cast<const uint4*>(orow + size_t(p) * pstride * kDC);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -341,7 +353,7 @@ void combine_out_proj_row_kernel(CombineProjArgs a) {
     }
   }
 
-  // ---- 3. merge the four waves (thread = 2 channels) ----
+  // ---- 3. merge each row's waves (thread = 2 channels of every row) ----
   *reinterpret_cast<float4*>(&sm.acc[wave][8 * lane]) = float4{acc[0], acc[1], acc[2], acc[3]};
   *reinterpret_cast<float4*>(&sm.acc[wave][8 * lane + 4]) = float4{acc[4], acc[5], acc[6], acc[7]};
   if (lane == 0) {
@@ -349,47 +361,56 @@ void combine_out_proj_row_kernel(CombineProjArgs a) {
     sm.sw[wave] = swv;
   }
   lds_barrier();
-  float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kNT / kWave; ++w) M = fmaxf(M, sm.mw[w]);
-  float tot = 0.f, u0 = 0.f, u1 = 0.f;
+  for (int qq = 0; qq < kRPW; ++qq) {
+    if (qq >= nr) break;  // (workgroup-uniform)
+    float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kNT / kWave; ++w) {
-    const float scw = sm.mw[w] == -INFINITY ? 0.f : expf(sm.mw[w] - M);
-    tot += sm.sw[w] * scw;
-    u0 += sm.acc[w][2 * tid] * scw;
-    u1 += sm.acc[w][2 * tid + 1] * scw;
+    for (int w = qq * kWPR; w < (qq + 1) * kWPR; ++w) M = fmaxf(M, sm.mw[w]);
+    float tot = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll
+    for (int w = qq * kWPR; w < (qq + 1) * kWPR; ++w) {
+      const float scw = sm.mw[w] == -INFINITY ? 0.f : expf(sm.mw[w] - M);
+      tot += sm.sw[w] * scw;
+      u0 += sm.acc[w][2 * tid] * scw;
+      u1 += sm.acc[w][2 * tid + 1] * scw;
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    const uint32_t pk = pack_bf16x2(u0 * inv, u1 * inv);
+    reinterpret_cast<uint32_t*>(sm.u[qq])[tid] = pk;
+    const size_t orow_out = size_t(r0 + qq) * H + h;  // (b * n_q + j) * H + h
+    if (a.u) reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.u) + orow_out * kDC)[tid] = pk;
+    if (a.lse_out && tid == 0) a.lse_out[orow_out] = tot > 0.f ? M + logf(tot) : -INFINITY;
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  const uint32_t pk = pack_bf16x2(u0 * inv, u1 * inv);
-  reinterpret_cast<uint32_t*>(sm.u)[tid] = pk;
-  const size_t orow_out = size_t(r) * H + h;  // (b * n_q + j) * H + h
-  if (a.u) reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.u) + orow_out * kDC)[tid] = pk;
-  if (a.lse_out && tid == 0) a.lse_out[orow_out] = tot > 0.f ? M + logf(tot) : -INFINITY;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows have landed
-  __syncthreads();                                  // u row and all W rows visible
+  __syncthreads();                                  // u rows and all W rows visible
 
   // ---- 4. o[r, h, v] = W^UV_i[v] . u (two threads per output) ----
   const int v = tid >> 1, half = tid & 1;
   if (v < dv) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) const u32x4 lds_u4;
-    const uint32_t wb = lds_addr(sm.w), ub = lds_addr(sm.u);
-    float d = 0.f;
-#pragma unroll 8
-    for (int x = 0; x < kDC / 16; ++x) {
-      const int xc = (kDC / 16) * half + x;  // 16-byte chunk of channels
-      const u32x4 wv = *(lds_u4*)(uintptr_t)(wb + chunk_off(v, xc));
-      const u32x4 uv = *(lds_u4*)(uintptr_t)(ub + xc * 16);
-      const uint32_t wa[4] = {wv[0], wv[1], wv[2], wv[3]}, ua[4] = {uv[0], uv[1], uv[2], uv[3]};
+    const uint32_t wb = lds_addr(sm.w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        d = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(ua[e] << 16), d);
-        d = fmaf(__uint_as_float(wa[e] & 0xffff0000u), __uint_as_float(ua[e] & 0xffff0000u), d);
+    for (int qq = 0; qq < kRPW; ++qq) {
+      if (qq >= nr) break;
+      const uint32_t ub = lds_addr(sm.u[qq]);
+      float d = 0.f;
+#pragma unroll 8
+      for (int x = 0; x < kDC / 16; ++x) {
+        const int xc = (kDC / 16) * half + x;  // 16-byte chunk of channels
+        const u32x4 wv = *(lds_u4*)(uintptr_t)(wb + chunk_off(v, xc));
+        const u32x4 uv = *(lds_u4*)(uintptr_t)(ub + xc * 16);
+        const uint32_t wa[4] = {wv[0], wv[1], wv[2], wv[3]}, ua[4] = {uv[0], uv[1], uv[2], uv[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(ua[e] << 16), d);
+          d = fmaf(__uint_as_float(wa[e] & 0xffff0000u), __uint_as_float(ua[e] & 0xffff0000u), d);
+        }
       }
+      d += __shfl_xor(d, 1, 64);
+      if (half == 0) static_cast<__bf16*>(a.out)[(size_t(r0 + qq) * H + h) * dv + v] = (__bf16)d;
     }
-    d += __shfl_xor(d, 1, 64);
-    if (half == 0) static_cast<__bf16*>(a.out)[orow_out * dv + v] = (__bf16)d;
   }
 }
 
@@ -404,12 +425,18 @@ bool combine_out_proj_supported(const CombineProjArgs& a) {
 hipError_t launch_combine_out_proj(const CombineProjArgs& a, hipStream_t st) {
   hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(combine_out_proj_kernel), int(sizeof(Smem)));
   if (e == hipSuccess)
-    e = ensure_dynamic_lds(reinterpret_cast<const void*>(combine_out_proj_row_kernel), int(sizeof(RowSmem)));
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(combine_out_proj_row_kernel<1>), int(sizeof(RowSmem)));
+  if (e == hipSuccess)
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(combine_out_proj_row_kernel<2>), int(sizeof(RowSmem)));
   if (e != hipSuccess) return e;
   const int R = a.batch * a.n_q;
-  if (R <= kMaxRowModeRows) {  // few rows: one workgroup per (head, row)
-    hipLaunchKernelGGL(combine_out_proj_row_kernel, dim3(unsigned(a.H) * unsigned(R)), dim3(kNT),
-                       sizeof(RowSmem), st, a);
+  if (R <= kMaxRowModeRows) {  // few rows: one workgroup per (head, one or two rows)
+    if (a.H * ((R + 1) / 2) >= 256)
+      hipLaunchKernelGGL(combine_out_proj_row_kernel<2>, dim3(unsigned(a.H) * unsigned((R + 1) / 2)), dim3(kNT),
+                         sizeof(RowSmem), st, a);
+    else
+      hipLaunchKernelGGL(combine_out_proj_row_kernel<1>, dim3(unsigned(a.H) * unsigned(R)), dim3(kNT),
+                         sizeof(RowSmem), st, a);
     return hipGetLastError();
   }
   // enough row groups per workgroup to keep about 256 workgroups (one per

@@ -863,6 +863,8 @@ FUSED = [
     (W.scaled(W.CONFIGS["ragged"], batch=5, len_lo=2, len_hi=3000), 64),    # up to ~30 pieces a row
     (W.scaled(W.CONFIGS["ragged"], batch=20, len_lo=2, len_hi=3000), 64),   # 40 rows, many pieces
     (W.scaled(W.CONFIGS["long"], batch=4, seq_len=16384), 256),             # 4 rows x 64 pieces
+    (W.scaled(W.CONFIGS["long"], batch=3, seq_len=5000), 96),               # 3 rows: two per workgroup, odd tail
+    (W.scaled(W.CONFIGS["long"], batch=1, seq_len=7000), 64),               # 1 row: one per workgroup
     # several 32-row groups per workgroup (the default above 96 rows): W^UV_i
     # loaded once and reused, per-group reads of the slot table
     (W.scaled(W.CONFIGS["v3"], batch=128, seq_len=200), 0),                 # 128 rows: 2 groups each
