@@ -323,24 +323,23 @@ void combine_out_proj_row_kernel(CombineProjArgs a) {
       x[s] = *reinterpret_cast<const uint4*>(orow + size_t(p) * pstride * kDC);
     }
     __builtin_amdgcn_sched_barrier(0);
-    float ls[kPC];
-#pragma unroll
-    for (int s = 0; s < kPC; ++s) {
-      ls[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse_l), s));
-      if (k0 + s >= npw) ls[s] = -INFINITY;
-    }
-    float mc = ls[0];
-#pragma unroll
-    for (int s = 1; s < kPC; ++s) mc = fmaxf(mc, ls[s]);
-    const float Mn = fmaxf(Mw, mc);
+    // the chunk's weights one piece per lane (lanes 0 .. kPC - 1; the rest
+    // repeat them), read back per piece
+    const float ls_l = k0 + lane % kPC < npw ? lse_l : -INFINITY;
+    float mc = fmaxf(ls_l, __shfl_xor(ls_l, 1, kWave));
+    mc = fmaxf(mc, __shfl_xor(mc, 2, kWave));
+    const float Mn = fmaxf(Mw, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mc))));
     const float sc = Mw == -INFINITY ? 0.f : expf(Mw - Mn);
+    const float w_l = ls_l == -INFINITY ? 0.f : expf(ls_l - Mn);
     Mw = Mn;
-    swv *= sc;
+    if (k0 > 0) {  // (the first chunk finds zeros: nothing to rescale)
+      swv *= sc;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+      for (int e = 0; e < 8; ++e) acc[e] *= sc;
+    }
 #pragma unroll
     for (int s = 0; s < kPC; ++s) {
-      const float w = ls[s] == -INFINITY ? 0.f : expf(ls[s] - Mn);
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), s));
       swv += w;
       if (w != 0.f) {
         const uint32_t v[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
