@@ -415,8 +415,9 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-  const int g = lane / 32;       // lane group: which 8-wide half of a 16-wide k step
-  const int hl = lane % 32;      // head within the wave (S^T / O^T column)
+  // Notation below: lane (g, hl) with g = lane / 32 (which 8-wide half of a
+  // 16-wide k step) and hl = lane % 32 (the head within the wave: the S^T /
+  // O^T column).
 
   // XCD-aware mapping: consecutive logical ids share an XCD (workgroups are
   // dealt round-robin to the 8 XCDs), so the n_q workgroups of a partition and
