@@ -441,9 +441,8 @@ void decode_mfma_kernel(DecodeArgs a) {
     const int gg = l >> 5, hh = (l >> 4) & 1, ss = l & 15;
     return uint32_t(step_off(4 * gg + (ss >> 2), 2 * hh + ((ss & 3) >> 1)) + 8 * (ss & 1));
   };
-  // bf16: kept in two registers for the whole kernel.  fp8: recomputed from
-  // a fresh lane id at every step -- two registers fewer across the loop,
-  // which the dequantisation needs to stay spill-free.
+  // (mode 2's V offsets, from a 64-byte-row layout; recomputed from a fresh
+  // lane id at every step: no register across the loop)
   auto voff0_of8 = [](int l) __attribute__((always_inline)) {
     const int gg = l >> 5, hh = (l >> 4) & 1, ss = l & 15;
     return uint32_t(v8_off(4 * gg + (ss >> 2), 2 * hh + ((ss & 3) >> 1)) + 8 * (ss & 1));
@@ -456,12 +455,11 @@ void decode_mfma_kernel(DecodeArgs a) {
     return uint32_t(t * 64 + (((2 * (l >> 5)) ^ cswz(t)) << 4));
   };
   const uint32_t koff0 = koff0_of(lane), voff0 = voff0_of(lane);
-  auto koff0_at = [&]() __attribute__((always_inline)) {
-    if constexpr (kF8) return koff0_of(tid_fresh() & (kWave - 1)); else return koff0;
-  };
-  auto voff0_at = [&]() __attribute__((always_inline)) {
-    if constexpr (kF8) return voff0_of(tid_fresh() & (kWave - 1)); else return voff0;
-  };
+  // kept in two registers across the step loop (the bf16 and the any-scale
+  // loops; recomputing them from a fresh lane id each step costs the
+  // instruction-bound loop more than the two registers)
+  auto koff0_at = [&]() __attribute__((always_inline)) { return koff0; };
+  auto voff0_at = [&]() __attribute__((always_inline)) { return voff0; };
   const int loff = load_lane_off(lane, wave & 1);
   // Lane id for the fp8 modes' per-step lane arithmetic: mode 1 recomputes it
   // from a fresh thread id (registers across its loop are short), mode 2 --
