@@ -461,17 +461,12 @@ void decode_mfma_kernel(DecodeArgs a) {
   auto koff0_at = [&]() __attribute__((always_inline)) { return koff0; };
   auto voff0_at = [&]() __attribute__((always_inline)) { return voff0; };
   const int loff = load_lane_off(lane, wave & 1);
-  // Lane id for the fp8 modes' per-step lane arithmetic: mode 1 recomputes it
-  // from a fresh thread id (registers across its loop are short), mode 2 --
-  // whose Q takes half the registers -- lets the compiler keep the derived
-  // offsets across the loop instead of recomputing them every step.
-  auto lane8 = [&]() __attribute__((always_inline)) {
-    if constexpr (kP2) return lane; else return tid_fresh() % kWave;
-  };
-  // mode 2: this lane's source chunk in its code loads (token 16 (wave % 2) + lane / 4)
+  // mode 2: this lane's source chunk in its code loads (token 16 (wave % 2) +
+  // lane / 4); from the plain lane id, so the compiler keeps it across the
+  // step loop instead of recomputing it for each of a step's loads
   auto loff8_at = [&]() __attribute__((always_inline)) {
-    const int l = lane8(), t = 16 * (wave & 1) + l / 4;
-    return t * kD + (((l & 3) ^ cswz(t)) << 4);
+    const int t = 16 * (wave & 1) + lane / 4;
+    return t * kD + (((lane & 3) ^ cswz(t)) << 4);
   };
 
   // Speculative Q: with equal lengths, partition `part`'s first piece belongs
@@ -936,7 +931,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         run_step(std::true_type{}, std::true_type{}, h, [&](int n) __attribute__((always_inline)) {
           if (n == 2 && nx) blk_raw = sm.ptab[((h + 3) >> 1) - pbase];
         }, [&](int n) __attribute__((always_inline)) {
-          if (n % 6 == 2) load_piece_p2(rc, rs, dst, wave, loff8_at(), lane8(), n / 6);
+          if (n % 6 == 2) load_piece_p2(rc, rs, dst, wave, loff8_at(), lane, n / 6);
         });
       }
       step_barrier();  // V of the last step is complete
